@@ -1,0 +1,220 @@
+"""CPU oracle for GQA attention with a learned per-head sink logit.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package; the product path
+(``gqa_attention_sinks_prefill_amd``) never does, and the two share no code.
+
+The arithmetic lives in ``sink_oracle.c`` (fp64, OpenMP, two-pass softmax over
+``[sink_h, scale * q.k_j]`` followed by a weighted sum of V; the sink has no
+value row).  Its header cites the passages of "GPT-OSS on day 0" (section
+"Kernels for GPT-OSS / Sink-Attention") and "Hosting Qwen on Blackwell"
+(section "Deployment on GB200 NVL72", HND cache order) that it follows.  This
+module only builds the shared object with gcc, marshals torch CPU tensors into
+pointers and strides, and returns numpy float64 arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sink_oracle.c")
+_LIB = os.path.join(_HERE, "libsinkoracle.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int
+_F64 = ctypes.c_double
+
+
+def build(verbose: bool = False) -> str:
+    """Compile sink_oracle.c into libsinkoracle.so (gcc, -O2, OpenMP, no fast-math)."""
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-o", tmp, _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    lib.oracle_prefill.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                   _P, _P, _I32, _I32, _I32, _I32, _F64, _I32,
+                                   _P, _I64, _I32, _P, _P, _P]
+    lib.oracle_prefill.restype = _I32
+    lib.oracle_decode.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I64, _I64,
+                                  _P, _I32, _P, _I32, _I32, _I32, _F64,
+                                  _P, _I64, _I32, _P, _P, _P]
+    lib.oracle_decode.restype = _I32
+    lib.oracle_chunk_states.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I64, _I64,
+                                        _P, _I32, _P, _I32, _I32, _I32, _F64,
+                                        _I32, _I32, _I32, _P, _I64, _I32, _P, _P, _P]
+    lib.oracle_chunk_states.restype = _I32
+    lib.oracle_merge_states.argtypes = [_P, _P, _P, _I64, _I32, _I32, _P, _P]
+    lib.oracle_merge_states.restype = _I32
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: the process's CPU affinity, capped by OMP_NUM_THREADS."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def _bf16(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype != torch.bfloat16 or t.device.type != "cpu":
+        raise TypeError("oracle inputs must be bfloat16 CPU tensors")
+    if t.stride(-1) != 1:
+        raise ValueError("oracle inputs need unit stride along head_dim")
+    return t
+
+
+def _rows(rows, n_default):
+    if rows is None:
+        return None, n_default
+    arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    return arr, arr.shape[0]
+
+
+def _ptr(a) -> int | None:
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    return a.data_ptr()
+
+
+def prefill(q, k, v, sinks, cu_seqlens, *, causal=True, scale=None, rows=None,
+            kv_layout="hnd", threads=None):
+    """Sink attention over packed sequences.
+
+    q: [T, Hq, D] bf16; k, v: bf16, [Hkv, T, D] for kv_layout="hnd" (heads
+    leading, tokens contiguous) or [T, Hkv, D] for "nhd"; any strides with
+    unit stride along D.  sinks: [Hq] fp32; cu_seqlens: [S+1] int32.
+    rows: optional iterable of (token, head) pairs; default all, token-major.
+    Returns (o [n, D], lse [n], sink_share [n]) as float64 numpy arrays.
+    """
+    q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    T, Hq, D = q.shape
+    k_st, k_sh, Hkv = _kv_strides(k, kv_layout)
+    v_st, v_sh, _ = _kv_strides(v, kv_layout)
+    sinks = sinks.to(torch.float32).contiguous()
+    cu = cu_seqlens.to(torch.int32).contiguous()
+    rows_arr, n = _rows(rows, T * Hq)
+    o = np.zeros((n, D), np.float64)
+    lse = np.zeros(n, np.float64)
+    share = np.zeros(n, np.float64)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = _load().oracle_prefill(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k_st, k_sh,
+        v.data_ptr(), v_st, v_sh, sinks.data_ptr(), cu.data_ptr(), cu.numel() - 1,
+        Hq, Hkv, D, scale, int(bool(causal)), _ptr(rows_arr), n,
+        threads or default_threads(), o.ctypes.data, lse.ctypes.data, share.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_prefill rejected its arguments")
+    return o, lse, share
+
+
+def _kv_strides(t: torch.Tensor, layout: str):
+    """(token stride, head stride, Hkv) of a 3-D K/V tensor in HND or NHD order."""
+    if t.dim() != 3:
+        raise ValueError("K/V must be 3-D")
+    if layout == "hnd":
+        return t.stride(1), t.stride(0), t.shape[0]      # [Hkv, T, D]
+    if layout == "nhd":
+        return t.stride(0), t.stride(1), t.shape[1]      # [T, Hkv, D]
+    raise ValueError("kv_layout must be 'hnd' or 'nhd'")
+
+
+def decode(q, k_cache, v_cache, seq_lens, sinks, *, scale=None, rows=None, threads=None):
+    """Sink attention of one query token per request over an HND cache.
+
+    q: [B, Hq, D] bf16; k_cache, v_cache: [B, Hkv, max_ctx, D] bf16 (any
+    strides with unit d-stride, both caches sharing them); seq_lens: [B] int32.
+    Returns (o [n, D], lse [n], sink_share [n]) float64, rows (b, h) b-major.
+    """
+    q, k_cache, v_cache = _bf16(q), _bf16(k_cache), _bf16(v_cache)
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("K and V caches must share strides")
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    sinks = sinks.to(torch.float32).contiguous()
+    lens = seq_lens.to(torch.int32).contiguous()
+    rows_arr, n = _rows(rows, B * Hq)
+    o = np.zeros((n, D), np.float64)
+    lse = np.zeros(n, np.float64)
+    share = np.zeros(n, np.float64)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = _load().oracle_decode(
+        q.data_ptr(), q.stride(0), q.stride(1), k_cache.data_ptr(), v_cache.data_ptr(),
+        k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), lens.data_ptr(), B,
+        sinks.data_ptr(), Hq, Hkv, D, scale, _ptr(rows_arr), n,
+        threads or default_threads(), o.ctypes.data, lse.ctypes.data, share.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_decode rejected its arguments")
+    return o, lse, share
+
+
+def chunk_states(q, k_cache, v_cache, seq_lens, sinks, split_size, num_splits, *,
+                 sink_chunk=0, scale=None, rows=None, threads=None):
+    """Per-chunk (o, m, d) states of decode rows; m in natural-log units.
+
+    Returns o [n, num_splits, D], m [n, num_splits], d [n, num_splits].
+    sink_chunk selects which chunk carries the sink (-1: all of them, wrong
+    on purpose, used only as a negative control).
+    """
+    q, k_cache, v_cache = _bf16(q), _bf16(k_cache), _bf16(v_cache)
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("K and V caches must share strides")
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    sinks = sinks.to(torch.float32).contiguous()
+    lens = seq_lens.to(torch.int32).contiguous()
+    rows_arr, n = _rows(rows, B * Hq)
+    o = np.zeros((n, num_splits, D), np.float64)
+    m = np.zeros((n, num_splits), np.float64)
+    d = np.zeros((n, num_splits), np.float64)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = _load().oracle_chunk_states(
+        q.data_ptr(), q.stride(0), q.stride(1), k_cache.data_ptr(), v_cache.data_ptr(),
+        k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), lens.data_ptr(), B,
+        sinks.data_ptr(), Hq, Hkv, D, scale, int(split_size), int(num_splits),
+        int(sink_chunk), _ptr(rows_arr), n, threads or default_threads(),
+        o.ctypes.data, m.ctypes.data, d.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_chunk_states rejected its arguments")
+    return o, m, d
+
+
+def merge_states(o_parts, m_parts, d_parts):
+    """Merge chunk states: o [n, S, D], m/d [n, S] float64 -> (o [n, D], lse [n])."""
+    o_parts = np.ascontiguousarray(o_parts, np.float64)
+    m_parts = np.ascontiguousarray(m_parts, np.float64)
+    d_parts = np.ascontiguousarray(d_parts, np.float64)
+    n, S, D = o_parts.shape
+    o = np.zeros((n, D), np.float64)
+    lse = np.zeros(n, np.float64)
+    rc = _load().oracle_merge_states(o_parts.ctypes.data, m_parts.ctypes.data,
+                                     d_parts.ctypes.data, n, S, D, o.ctypes.data,
+                                     lse.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_merge_states rejected its arguments")
+    return o, lse

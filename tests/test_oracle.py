@@ -1,0 +1,290 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself.
+
+Sources of truth, none of which is the oracle's own formula typed again:
+* a library routine: torch's scaled_dot_product_attention in float64 on CPU
+  (a -inf sink must reduce sink attention to it exactly; a finite sink must
+  equal it over one extra all-zero key whose column carries the sink as an
+  additive mask);
+* closed forms (identical keys; a single visible key; the sink share);
+* invariants (split-then-merge equals unsplit for every chunk size, with a
+  negative control; GQA equals MHA over repeated K/V; key permutation).
+
+A plausible slip in the oracle -- a dropped sink term, the sink scaled by the
+softmax scale, j < i instead of j <= i, the wrong GQA grouping, the sink in
+every chunk -- fails at least one test here.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+
+def _bf16_randn(g, *shape, scale=1.0):
+    return (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16)
+
+
+def _sdpa(q, k, v, *, causal, scale, mask=None):
+    """float64 SDPA; q [H, L, D], k/v [H, S, D] (already expanded over GQA)."""
+    return F.scaled_dot_product_attention(
+        q.double().unsqueeze(0), k.double().unsqueeze(0), v.double().unsqueeze(0),
+        attn_mask=None if mask is None else mask.unsqueeze(0), is_causal=causal,
+        scale=scale).squeeze(0)
+
+
+def _packed_prefill(g, lens, Hq, Hkv, D):
+    cu = torch.zeros(len(lens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lens), 0)
+    T = int(cu[-1])
+    q = _bf16_randn(g, T, Hq, D)
+    k = _bf16_randn(g, Hkv, T, D)
+    v = _bf16_randn(g, Hkv, T, D)
+    return q, k, v, cu
+
+
+# ---------------------------------------------------------------- P1 ------
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 1, 8), (6, 2, 4), (8, 8, 64), (8, 2, 64)])
+def test_neg_inf_sink_is_standard_attention_prefill(causal, Hq, Hkv, D):
+    g = torch.Generator().manual_seed(11 + Hq + D)
+    lens = [1, 5, 17, 33]
+    q, k, v, cu = _packed_prefill(g, lens, Hq, Hkv, D)
+    sinks = torch.full((Hq,), float("-inf"))
+    scale = 1.0 / math.sqrt(D)
+    o, _, share = oracle.prefill(q, k, v, sinks, cu, causal=causal, scale=scale)
+    o = o.reshape(-1, Hq, D)
+    r = Hq // Hkv
+    for s in range(len(lens)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        qs = q[a:b].transpose(0, 1)                              # [Hq, L, D]
+        ks = k[:, a:b].repeat_interleave(r, dim=0)               # contiguous groups
+        vs = v[:, a:b].repeat_interleave(r, dim=0)
+        ref = _sdpa(qs, ks, vs, causal=causal, scale=scale).transpose(0, 1)
+        np.testing.assert_allclose(o[a:b], ref.numpy(), rtol=0, atol=1e-12)
+    assert np.all(share == 0.0)
+
+
+def test_neg_inf_sink_is_standard_attention_decode():
+    g = torch.Generator().manual_seed(5)
+    B, Hq, Hkv, D, max_ctx = 3, 8, 2, 16, 40
+    lens = torch.tensor([40, 1, 23], dtype=torch.int32)
+    q = _bf16_randn(g, B, Hq, D)
+    kc = _bf16_randn(g, B, Hkv, max_ctx, D)
+    vc = _bf16_randn(g, B, Hkv, max_ctx, D)
+    sinks = torch.full((Hq,), float("-inf"))
+    o, _, _ = oracle.decode(q, kc, vc, lens, sinks)
+    o = o.reshape(B, Hq, D)
+    for b in range(B):
+        L = int(lens[b])
+        ks = kc[b, :, :L].repeat_interleave(Hq // Hkv, dim=0)
+        vs = vc[b, :, :L].repeat_interleave(Hq // Hkv, dim=0)
+        ref = _sdpa(q[b].unsqueeze(1), ks, vs, causal=False, scale=1 / math.sqrt(D))
+        np.testing.assert_allclose(o[b], ref[:, 0].numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P5 ------
+@pytest.mark.parametrize("causal", [True, False])
+def test_sink_is_an_extra_zero_key_with_additive_mask(causal):
+    """A finite sink equals SDPA over n+1 keys: an all-zero key (logit 0) with
+    a zero value row, whose column gets the raw sink as an additive mask."""
+    g = torch.Generator().manual_seed(7)
+    Hq, Hkv, D, L = 8, 2, 32, 29
+    q, k, v, cu = _packed_prefill(g, [L], Hq, Hkv, D)
+    sinks = torch.empty(Hq).uniform_(-4, 4, generator=g)
+    sinks[3] = 20.0
+    scale = 1.0 / math.sqrt(D)
+    o, _, _ = oracle.prefill(q, k, v, sinks, cu, causal=causal, scale=scale)
+    o = o.reshape(L, Hq, D)
+    r = Hq // Hkv
+    qs = q.transpose(0, 1)
+    ks = torch.cat([torch.zeros(Hkv, 1, D, dtype=k.dtype), k], 1).repeat_interleave(r, 0)
+    vs = torch.cat([torch.zeros(Hkv, 1, D, dtype=v.dtype), v], 1).repeat_interleave(r, 0)
+    mask = torch.zeros(Hq, L, L + 1, dtype=torch.float64)
+    mask[:, :, 0] = sinks.double()[:, None]
+    if causal:   # key j+1 of the extended set is visible to row i iff j <= i
+        mask[:, :, 1:] = torch.triu(torch.full((L, L), float("-inf"), dtype=torch.float64), 1)
+    ref = _sdpa(qs, ks, vs, causal=False, scale=scale, mask=mask).transpose(0, 1)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P2 ------
+@pytest.mark.parametrize("n", [1, 2, 7, 64])
+@pytest.mark.parametrize("sink", [-3.0, 0.0, 1.5, 20.0])
+def test_identical_keys_closed_form(n, sink):
+    """n copies of one key/value: o = n e^x / (n e^x + e^s) * v with x = scale q.k."""
+    D = 8
+    qv = torch.tensor([1.0, -0.5, 0.25, 2.0, 0.0, 1.0, -1.0, 0.5])
+    kv = torch.tensor([0.5, 1.0, -2.0, 0.75, 3.0, -0.25, 0.5, 1.0])
+    vv = torch.tensor([1.0, 2.0, -3.0, 0.5, 0.0, -1.25, 4.0, 0.125])
+    q = qv.to(torch.bfloat16).reshape(1, 1, D)
+    kc = kv.to(torch.bfloat16).reshape(1, 1, 1, D).expand(1, 1, n, D).contiguous()
+    vc = vv.to(torch.bfloat16).reshape(1, 1, 1, D).expand(1, 1, n, D).contiguous()
+    scale = 0.5
+    o, lse, share = oracle.decode(q, kc, vc, torch.tensor([n], dtype=torch.int32),
+                                  torch.tensor([sink]), scale=scale)
+    x = scale * float(np.dot(qv.numpy().astype(np.float64), kv.numpy().astype(np.float64)))
+    w = n * math.exp(x) / (n * math.exp(x) + math.exp(sink))
+    np.testing.assert_allclose(o[0], w * vv.numpy().astype(np.float64), rtol=1e-13, atol=1e-300)
+    assert lse[0] == pytest.approx(math.log(n * math.exp(x) + math.exp(sink)), rel=1e-13)
+    assert share[0] == pytest.approx(1.0 - w, rel=1e-12, abs=1e-15)
+
+
+def test_first_causal_row_sees_only_key_zero():
+    """Row 0 of a causal prefill sees key 0 alone: o = e^x0/(e^x0+e^s) v0."""
+    g = torch.Generator().manual_seed(3)
+    q, k, v, cu = _packed_prefill(g, [9, 6], 2, 1, 16)
+    sinks = torch.tensor([0.7, -1.1])
+    o, _, _ = oracle.prefill(q, k, v, sinks, cu, causal=True, scale=0.25,
+                             rows=[(0, 0), (0, 1), (9, 1)])
+    for i, (t, h) in enumerate([(0, 0), (0, 1), (9, 1)]):
+        x0 = 0.25 * float(q[t, h].double() @ k[0, t].double())
+        p = math.exp(x0) / (math.exp(x0) + math.exp(float(sinks[h])))
+        np.testing.assert_allclose(o[i], p * v[0, t].double().numpy(), rtol=1e-13, atol=1e-300)
+
+
+# ---------------------------------------------------------------- P3 ------
+def test_sink_share_matches_logaddexp():
+    g = torch.Generator().manual_seed(9)
+    B, Hq, Hkv, D, L = 2, 4, 1, 64, 50
+    q = _bf16_randn(g, B, Hq, D)
+    kc = _bf16_randn(g, B, Hkv, L, D, scale=2.0)
+    vc = _bf16_randn(g, B, Hkv, L, D)
+    sinks = torch.tensor([-2.0, 0.0, 3.0, 20.0])
+    lens = torch.tensor([L, 13], dtype=torch.int32)
+    o_nos, lse_nos, _ = oracle.decode(q, kc, vc, lens, torch.full((Hq,), float("-inf")))
+    o, lse, share = oracle.decode(q, kc, vc, lens, sinks)
+    s = np.tile(sinks.double().numpy(), B)
+    # share = e^s / (e^s + sum e^x) = exp(s - logaddexp(s, lse_std))
+    np.testing.assert_allclose(share, np.exp(s - np.logaddexp(s, lse_nos)), rtol=1e-12)
+    np.testing.assert_allclose(lse, np.logaddexp(s, lse_nos), rtol=1e-13)
+    # ---------------------------------------------------------- P6 ------
+    # o_sink = sigmoid(lse_std - s) * o_std, row by row
+    sig = 1.0 / (1.0 + np.exp(s - lse_nos))
+    np.testing.assert_allclose(o, sig[:, None] * o_nos, rtol=0, atol=1e-13)
+    # the weights of the keys and the sink sum to one: sum_j p_j = 1 - share
+    rows = [(0, 1)]
+    o1, _, sh1 = oracle.decode(q, kc, torch.ones_like(vc), lens, sinks, rows=rows)
+    np.testing.assert_allclose(o1[0], np.full(D, 1.0 - sh1[0]), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- P4 ------
+def _decode_case(seed=21, n=37, D=8):
+    g = torch.Generator().manual_seed(seed)
+    q = _bf16_randn(g, 1, 2, D)
+    kc = _bf16_randn(g, 1, 1, n, D, scale=1.5)
+    vc = _bf16_randn(g, 1, 1, n, D)
+    sinks = torch.tensor([1.25, -0.5])
+    return q, kc, vc, torch.tensor([n], dtype=torch.int32), sinks
+
+
+def test_split_then_merge_equals_unsplit_every_chunk_size():
+    q, kc, vc, lens, sinks = _decode_case()
+    n = int(lens[0])
+    o_ref, lse_ref, _ = oracle.decode(q, kc, vc, lens, sinks)
+    for S in range(1, n + 1):
+        for extra in (0, 2):                     # trailing empty chunks too
+            ns = -(-n // S) + extra
+            o_p, m_p, d_p = oracle.chunk_states(q, kc, vc, lens, sinks, S, ns)
+            o, lse = oracle.merge_states(o_p, m_p, d_p)
+            np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12, err_msg=f"S={S}")
+            np.testing.assert_allclose(lse, lse_ref, rtol=1e-13, err_msg=f"S={S}")
+            if extra:
+                assert np.all(np.isneginf(m_p[:, -1])) and np.all(d_p[:, -1] == 0)
+
+
+def test_sink_in_any_single_chunk_is_equivalent():
+    q, kc, vc, lens, sinks = _decode_case(seed=4)
+    o_ref, _, _ = oracle.decode(q, kc, vc, lens, sinks)
+    for c in range(5):
+        o, _ = oracle.merge_states(*oracle.chunk_states(q, kc, vc, lens, sinks, 8, 5,
+                                                        sink_chunk=c))
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+
+
+def test_sink_in_every_chunk_is_wrong_negative_control():
+    """Seeding every chunk counts the sink k times: equal to sink + ln k, not sink."""
+    q, kc, vc, lens, sinks = _decode_case(seed=8)
+    o_ref, _, _ = oracle.decode(q, kc, vc, lens, sinks)
+    for k in (2, 3, 5):
+        S = -(-int(lens[0]) // k)
+        o_all, _ = oracle.merge_states(*oracle.chunk_states(q, kc, vc, lens, sinks, S, k,
+                                                            sink_chunk=-1))
+        o_shift, _, _ = oracle.decode(q, kc, vc, lens, sinks + math.log(k))
+        # sinks are fp32, so s + ln k is rounded to ~1e-7 relative before use
+        np.testing.assert_allclose(o_all, o_shift, rtol=0, atol=1e-8)
+        assert np.max(np.abs(o_all - o_ref)) > 1e-3
+
+
+def test_empty_request_and_empty_chunk_states():
+    q, kc, vc, _, _ = _decode_case(seed=2)
+    lens = torch.tensor([0], dtype=torch.int32)
+    sinks = torch.tensor([0.75, float("-inf")])
+    o, lse, share = oracle.decode(q, kc, vc, lens, sinks)
+    assert np.all(o == 0)
+    assert lse[0] == pytest.approx(0.75) and share[0] == 1.0
+    assert np.isneginf(lse[1]) and share[1] == 0.0
+    o_p, m_p, d_p = oracle.chunk_states(q, kc, vc, lens, sinks, 4, 3)
+    assert m_p[0, 0] == pytest.approx(0.75) and d_p[0, 0] == 1.0
+    assert np.all(np.isneginf(m_p[0, 1:])) and np.all(np.isneginf(m_p[1]))
+    o_m, lse_m = oracle.merge_states(o_p, m_p, d_p)
+    assert np.all(o_m == 0) and lse_m[0] == pytest.approx(0.75) and np.isneginf(lse_m[1])
+
+
+# ---------------------------------------------------------------- P7 ------
+def test_gqa_equals_mha_with_repeated_kv():
+    g = torch.Generator().manual_seed(13)
+    Hq, Hkv, D = 8, 2, 16
+    q, k, v, cu = _packed_prefill(g, [12, 30], Hq, Hkv, D)
+    sinks = torch.empty(Hq).uniform_(-4, 4, generator=g)
+    o_gqa, lse_gqa, _ = oracle.prefill(q, k, v, sinks, cu)
+    k_rep = k.repeat_interleave(Hq // Hkv, 0).contiguous()
+    v_rep = v.repeat_interleave(Hq // Hkv, 0).contiguous()
+    o_mha, lse_mha, _ = oracle.prefill(q, k_rep, v_rep, sinks, cu)
+    assert np.array_equal(o_gqa, o_mha) and np.array_equal(lse_gqa, lse_mha)
+
+
+# ---------------------------------------------------------------- P8 ------
+def test_decode_is_invariant_to_key_order():
+    g = torch.Generator().manual_seed(17)
+    B, Hq, Hkv, D, L = 1, 4, 2, 32, 45
+    q = _bf16_randn(g, B, Hq, D)
+    kc = _bf16_randn(g, B, Hkv, L, D)
+    vc = _bf16_randn(g, B, Hkv, L, D)
+    sinks = torch.tensor([0.5, -1.0, 3.0, -3.5])
+    lens = torch.tensor([L], dtype=torch.int32)
+    perm = torch.randperm(L, generator=g)
+    o, lse, _ = oracle.decode(q, kc, vc, lens, sinks)
+    o_p, lse_p, _ = oracle.decode(q, kc[:, :, perm].contiguous(), vc[:, :, perm].contiguous(),
+                                  lens, sinks)
+    np.testing.assert_allclose(o_p, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_p, lse, rtol=1e-14)
+
+
+def test_prefill_and_decode_agree_on_the_last_row():
+    """Decode over a cache equals the last causal row of the same prefill,
+    whether the prefill K/V is HND or NHD."""
+    g = torch.Generator().manual_seed(23)
+    Hq, Hkv, D, L = 4, 2, 64, 40
+    q, k, v, cu = _packed_prefill(g, [L], Hq, Hkv, D)
+    sinks = torch.tensor([-1.0, 0.0, 2.0, float("-inf")])
+    rows = [(L - 1, h) for h in range(Hq)]
+    o_p, lse_p, _ = oracle.prefill(q, k, v, sinks, cu, rows=rows)
+    o_n, lse_n, _ = oracle.prefill(q, k.transpose(0, 1).contiguous(),
+                                   v.transpose(0, 1).contiguous(), sinks, cu, rows=rows,
+                                   kv_layout="nhd")
+    o_d, lse_d, _ = oracle.decode(q[L - 1:L], k.unsqueeze(0), v.unsqueeze(0),
+                                  torch.tensor([L], dtype=torch.int32), sinks)
+    assert np.array_equal(o_p, o_d) and np.array_equal(lse_p, lse_d)
+    assert np.array_equal(o_p, o_n)
+
+
+def test_rejects_bad_rows():
+    g = torch.Generator().manual_seed(1)
+    q, k, v, cu = _packed_prefill(g, [4], 2, 1, 4)
+    with pytest.raises(ValueError):
+        oracle.prefill(q, k, v, torch.zeros(2), cu, rows=[(4, 0)])
+    with pytest.raises(ValueError):
+        oracle.prefill(q, k, v, torch.zeros(2), cu, rows=[(0, 2)])
