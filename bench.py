@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+One step = one pass over every row of the hot path on synthetic inputs that
+already sit in HBM:
+  * causal prefill of the GPT-OSS-shaped workload (one 8192-token sequence,
+    64 query / 8 KV heads, head_dim 64, bf16) -- sink_attn_prefill;
+  * split-KV decode of 64 requests x 8192 cached tokens (64 / 8 heads, d 64,
+    HND cache, 1024-token chunks) -- sink_attn_decode_split then
+    sink_attn_merge_states.
+All three kernels run back to back on torch's current stream; each launch is
+bracketed by HIP events on that stream.
+
+Printed: ONE JSON line.  `value` is prefill TFLOP/s (algorithmic flops: 4*D
+per visible causal (query, key) pair, i.e. 4*D*Hq*N(N+1)/2) over the prefill
+kernel's mean event-timed duration; the `decode` object carries the decode
+KV-read GB/s (K and V of every cached token read once per KV head) over the
+split + merge duration.  `roofline` compares the prefill kernel with the
+bf16 dense MFMA peak, `decode.roofline` the decode split kernel with the HBM
+peak.  `cpu_baseline` times the fp64 CPU oracle on a bounded random sample
+of prefill rows on this host, scaled to TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gqa_attention_sinks_prefill_amd as sa  # noqa: E402
+from gqa_attention_sinks_prefill_amd import workloads as wl  # noqa: E402
+
+# MI355X published peaks (dense): bf16 MFMA 256 CU x 2.4 GHz x 4096 flop/clk/CU,
+# HBM3E 8 TB/s.
+PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gqa_attention_sinks_prefill_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel sources as they are now (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = rec.get("kernels", {}).get(kernel)
+    return None if ent is None else ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(pre_inp, cfg, out_gpu, seconds: float, seed: int = 0):
+    """Time the fp64 oracle on random prefill rows for about `seconds`, and use
+    the same rows as a parity spot check of the timed GPU output."""
+    import oracle   # test infrastructure: only this leg of the benchmark uses it
+
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(seed)
+    T, Hq, D = pre_inp["q"].shape
+    done_rows, flops, elapsed = [], 0.0, 0.0
+    outs = []
+    batch = 256
+    while elapsed < seconds:
+        rows = np.stack([rng.integers(0, T, batch), rng.integers(0, Hq, batch)], 1)
+        t0 = time.perf_counter()
+        o, _, _ = oracle.prefill(pre_inp["q"], pre_inp["k"], pre_inp["v"], pre_inp["sinks"],
+                                 pre_inp["cu_seqlens"], causal=True, scale=cfg.scale,
+                                 rows=rows, threads=threads)
+        elapsed += time.perf_counter() - t0
+        flops += float(np.sum(4.0 * D * (rows[:, 0] + 1)))      # one sequence: pos = token
+        done_rows.append(rows)
+        outs.append(o)
+    rows = np.concatenate(done_rows)
+    ref = np.concatenate(outs)
+    got = out_gpu.detach().cpu()[torch.from_numpy(rows[:, 0]), torch.from_numpy(rows[:, 1])]
+    err = np.abs(got.double().numpy() - ref)
+    return ({"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
+             "kind": "oracle",
+             "sample": f"{len(rows)} random (token, head) rows of the 8192-token prefill, "
+                       f"{flops:.3g} algorithmic flop in {elapsed:.1f} s, fp64 C + OpenMP"},
+            {"rows": int(len(rows)), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+             "bound_max_abs": 2e-2, "bound_mean_abs": 2e-3})
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="host time budget of the oracle baseline (0 disables it)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    # ---- inputs, resident in HBM before timing ---------------------------------
+    pcfg, dcfg = wl.GPTOSS_PREFILL, wl.SPLIT_DECODE
+    pre = wl.prefill_inputs(pcfg)
+    dec = wl.decode_inputs(dcfg)
+    q, k, v = pre["q"].to(dev), pre["k"].to(dev), pre["v"].to(dev)
+    sinks_p, cu = pre["sinks"].to(dev), pre["cu_seqlens"].to(dev)
+    out = torch.empty_like(q)
+    dq, kc, vc = dec["q"].to(dev), dec["k_cache"].to(dev), dec["v_cache"].to(dev)
+    lens, sinks_d = dec["seq_lens"].to(dev), dec["sinks"].to(dev)
+    B, Hq, D = dq.shape
+    ns = dcfg.num_splits
+    po = torch.empty(B, Hq, ns, D, device=dev)
+    pm = torch.empty(B, Hq, ns, device=dev)
+    pd = torch.empty(B, Hq, ns, device=dev)
+    dout = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        sa.sink_attn_prefill(q, k, v, sinks_p, cu, pre["max_seqlen"], causal=True,
+                             scale=pcfg.scale, out=out, stream=stream)
+        if e: e[1].record(stream)
+        sa.sink_attn_decode_split(dq, kc, vc, lens, sinks_d, dcfg.split_size, ns,
+                                  scale=dcfg.scale, part_o=po, part_m=pm, part_d=pd,
+                                  stream=stream)
+        if e: e[2].record(stream)
+        sa.sink_attn_merge_states(po, pm, pd, out=dout, stream=stream)
+        if e: e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    split_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    merge_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    flops = wl.prefill_flops(pre["seqlens"].tolist(), pcfg.num_q_heads, pcfg.head_dim)
+    kv_bytes = wl.decode_kv_bytes(dec["seq_lens"].tolist(), dcfg.num_kv_heads, dcfg.head_dim)
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    dec_gbs = kv_bytes / ((split_ms + merge_ms) * 1e-3) / 1e9
+    split_gbs = kv_bytes / (split_ms * 1e-3) / 1e9
+
+    traffic_p = measured_traffic("prefill")
+    traffic_d = measured_traffic("decode_split")
+    res = {
+        "metric": "sink-attn prefill TFLOP/s & decode KV GB/s, % of MI355X roofline",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded randn / uniform inputs of the workload shapes; no weights)",
+        "config": {"workload": pcfg.name, "decode_workload": dcfg.name,
+                   "seq_len": 8192, "num_q_heads": 64, "num_kv_heads": 8, "head_dim": 64,
+                   "causal": True, "decode_batch": dcfg.batch, "decode_ctx": dcfg.ctx,
+                   "decode_split_size": dcfg.split_size, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_p, "kernel": "prefill_kernel<64,4>",
+                     "algorithmic_flop_per_launch": flops, "mean_launch_ms": round(pre_ms, 4)},
+        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "metric": "decode KV GB/s",
+                   "ms": round(split_ms + merge_ms, 4), "split_ms": round(split_ms, 4),
+                   "merge_ms": round(merge_ms, 4),
+                   "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                                "traffic": traffic_d, "kernel": "decode_split_kernel<64>",
+                                "algorithmic_bytes_per_launch": kv_bytes},
+                   "frac_of_hbm_peak_incl_merge": round(dec_gbs / PEAK_HBM_GBS, 4)},
+        "device": {"name": props.name, "compute_units": props.multi_processor_count,
+                   "gcn_arch": getattr(props, "gcnArchName", "")},
+    }
+    if args.cpu_seconds > 0:
+        cb, parity = cpu_baseline(pre, pcfg, out, args.cpu_seconds)
+        res["cpu_baseline"] = cb
+        res["parity_spot_check"] = parity
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+"""GQA attention with learned per-head sinks on MI355X (gfx950).
+
+Thin ctypes binding over ``libsinkattn.so`` (declared in ``include/sinkattn.h``).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor dtypes/devices, passes device pointers, element strides and
+the current HIP stream, and turns a non-zero return code into an exception.
+PyTorch is used for device memory and streams only.
+
+Entry points (same names as the C ABI):
+  sink_attn_prefill(q, k, v, sinks, cu_seqlens, max_seqlen, ...)
+  sink_attn_decode_split(q, k_cache, v_cache, seq_lens, sinks, split_size, ...)
+  sink_attn_merge_states(part_o, part_m, part_d, ...)
+and the convenience wrapper sink_attn_decode (split + merge on one stream).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge_states",
+           "sink_attn_decode", "SinkAttnError", "library_path", "load_library",
+           "EXPORTED_SYMBOLS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libsinkattn.so")
+_lib = None
+
+EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_decode_split",
+                    "sink_attn_merge_states", "sink_attn_last_error")
+
+
+class SinkAttnError(RuntimeError):
+    """A libsinkattn call returned a non-zero status."""
+
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsinkattn.so; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with "
+            "`python -m gqa_attention_sinks_prefill_amd.build_native` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    lib.sink_attn_prefill.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, I32, I32,
+                                      I32, I32, I32, F32, I32, P, I64, I64, P, P]
+    lib.sink_attn_prefill.restype = ctypes.c_int
+    lib.sink_attn_decode_split.argtypes = [P, I64, I64, P, P, I64, I64, I64, P, I32, I32, P,
+                                           I32, I32, I32, F32, I32, I32, P, P, P, P]
+    lib.sink_attn_decode_split.restype = ctypes.c_int
+    lib.sink_attn_merge_states.argtypes = [P, P, P, I32, I32, I32, I32, P, I64, I64, P, P]
+    lib.sink_attn_merge_states.restype = ctypes.c_int
+    lib.sink_attn_last_error.argtypes = []
+    lib.sink_attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        msg = load_library().sink_attn_last_error().decode(errors="replace")
+        raise SinkAttnError(fn, rc, msg)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, dim: int | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must be {dim}-D, got shape {tuple(t.shape)}")
+    return t
+
+
+def sink_attn_prefill(q, k, v, sinks, cu_seqlens, max_seqlen, *, causal=True, scale=None,
+                      kv_layout="hnd", out=None, lse=None, stream=None):
+    """Sink-attention prefill over packed sequences.
+
+    q: [T, Hq, D] bf16.  k, v: bf16 [Hkv, T, D] for kv_layout="hnd" (default)
+    or [T, Hkv, D] for "nhd"; any strides with unit stride along D.
+    sinks: [Hq] fp32.  cu_seqlens: [S+1] int32 on the GPU.  max_seqlen: int.
+    Returns out [T, Hq, D] bf16 (allocated if not given); fills lse [T, Hq]
+    fp32 when passed.
+    """
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(k, "k", torch.bfloat16, 3)
+    _dev(v, "v", torch.bfloat16, 3)
+    _dev(sinks, "sinks", torch.float32, 1)
+    _dev(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    T, Hq, D = q.shape
+    if kv_layout == "hnd":
+        Hkv = k.shape[0]
+        (k_sh, k_st), (v_sh, v_st) = k.stride()[:2], v.stride()[:2]
+    elif kv_layout == "nhd":
+        Hkv = k.shape[1]
+        (k_st, k_sh), (v_st, v_sh) = k.stride()[:2], v.stride()[:2]
+    else:
+        raise ValueError("kv_layout must be 'hnd' or 'nhd'")
+    if q.stride(2) != 1 or k.stride(2) != 1 or v.stride(2) != 1:
+        raise ValueError("q, k, v need unit stride along head_dim")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    _dev(out, "out", torch.bfloat16, 3)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, 2)
+        if not lse.is_contiguous() or tuple(lse.shape) != (T, Hq):
+            raise ValueError("lse must be a contiguous [T, Hq] fp32 tensor")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().sink_attn_prefill(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k_st, k_sh,
+        v.data_ptr(), v_st, v_sh, sinks.data_ptr(), cu_seqlens.data_ptr(),
+        cu_seqlens.numel() - 1, int(max_seqlen), Hq, Hkv, D, scale, int(bool(causal)),
+        out.data_ptr(), out.stride(0), out.stride(1),
+        lse.data_ptr() if lse is not None else None, _stream(stream))
+    _check("sink_attn_prefill", rc)
+    return out
+
+
+def sink_attn_decode_split(q, k_cache, v_cache, seq_lens, sinks, split_size, num_splits=None,
+                           *, max_ctx=None, scale=None, part_o=None, part_m=None, part_d=None,
+                           stream=None):
+    """Per-chunk decode states over an HND cache [B, Hkv, max_ctx, D].
+
+    Returns (part_o [B, Hq, S, D], part_m [B, Hq, S], part_d [B, Hq, S]) fp32.
+    """
+    _dev(q, "q", torch.bfloat16, 3)
+    _dev(k_cache, "k_cache", torch.bfloat16, 4)
+    _dev(v_cache, "v_cache", torch.bfloat16, 4)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    _dev(sinks, "sinks", torch.float32, 1)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if q.stride(2) != 1 or k_cache.stride(3) != 1:
+        raise ValueError("q and the caches need unit stride along head_dim")
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    max_ctx = k_cache.shape[2] if max_ctx is None else int(max_ctx)
+    if num_splits is None:
+        num_splits = -(-max_ctx // split_size)
+    shape = (B, Hq, num_splits)
+    if part_o is None:
+        part_o = torch.empty(*shape, D, dtype=torch.float32, device=q.device)
+        part_m = torch.empty(shape, dtype=torch.float32, device=q.device)
+        part_d = torch.empty(shape, dtype=torch.float32, device=q.device)
+    for t, nm, shp in ((part_o, "part_o", shape + (D,)), (part_m, "part_m", shape),
+                       (part_d, "part_d", shape)):
+        _dev(t, nm, torch.float32)
+        if not t.is_contiguous() or tuple(t.shape) != shp:
+            raise ValueError(f"{nm} must be contiguous with shape {shp}")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().sink_attn_decode_split(
+        q.data_ptr(), q.stride(0), q.stride(1), k_cache.data_ptr(), v_cache.data_ptr(),
+        k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), seq_lens.data_ptr(), B,
+        max_ctx, sinks.data_ptr(), Hq, Hkv, D, scale, int(split_size), int(num_splits),
+        part_o.data_ptr(), part_m.data_ptr(), part_d.data_ptr(), _stream(stream))
+    _check("sink_attn_decode_split", rc)
+    return part_o, part_m, part_d
+
+
+def sink_attn_merge_states(part_o, part_m, part_d, *, out=None, lse=None, stream=None):
+    """Merge chunk states [B, Hq, S, D] into out [B, Hq, D] bf16 (and lse [B, Hq])."""
+    _dev(part_o, "part_o", torch.float32, 4)
+    _dev(part_m, "part_m", torch.float32, 3)
+    _dev(part_d, "part_d", torch.float32, 3)
+    B, Hq, S, D = part_o.shape
+    for t, nm in ((part_o, "part_o"), (part_m, "part_m"), (part_d, "part_d")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if tuple(part_m.shape) != (B, Hq, S) or tuple(part_d.shape) != (B, Hq, S):
+        raise ValueError("part_m / part_d must be [B, Hq, S]")
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=part_o.device)
+    _dev(out, "out", torch.bfloat16, 3)
+    if out.stride(2) != 1:
+        raise ValueError("out needs unit stride along head_dim")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if not lse.is_contiguous() or lse.numel() != B * Hq:
+            raise ValueError("lse must be a contiguous [B, Hq] fp32 tensor")
+    rc = load_library().sink_attn_merge_states(
+        part_o.data_ptr(), part_m.data_ptr(), part_d.data_ptr(), B, Hq, S, D,
+        out.data_ptr(), out.stride(0), out.stride(1),
+        lse.data_ptr() if lse is not None else None, _stream(stream))
+    _check("sink_attn_merge_states", rc)
+    return out
+
+
+def sink_attn_decode(q, k_cache, v_cache, seq_lens, sinks, split_size, num_splits=None, *,
+                     max_ctx=None, scale=None, out=None, lse=None, partials=None, stream=None):
+    """Split-KV decode: sink_attn_decode_split then sink_attn_merge_states, same stream."""
+    po, pm, pd = partials if partials is not None else (None, None, None)
+    po, pm, pd = sink_attn_decode_split(q, k_cache, v_cache, seq_lens, sinks, split_size,
+                                        num_splits, max_ctx=max_ctx, scale=scale, part_o=po,
+                                        part_m=pm, part_d=pd, stream=stream)
+    return sink_attn_merge_states(po, pm, pd, out=out, lse=lse, stream=stream)

@@ -1,0 +1,203 @@
+// C ABI of libsinkattn.so: argument validation (host only, before any HIP
+// call), launch-shape selection, and error reporting.  The operations and
+// their layouts are documented in include/sinkattn.h.
+#include "sinkattn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+bool stride_ok(int64_t s) { return s >= 0 && s % 8 == 0; }
+
+int check_heads(int32_t hq, int32_t hkv, int32_t d) {
+  if (hq <= 0 || hkv <= 0) return fail(SINK_ATTN_EINVAL, "head counts must be positive (Hq=%d, Hkv=%d)", hq, hkv);
+  if (hq % hkv != 0) return fail(SINK_ATTN_EINVAL, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", hq, hkv);
+  if (d != 64 && d != 128) return fail(SINK_ATTN_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", d);
+  return SINK_ATTN_OK;
+}
+
+int check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(SINK_ATTN_EINVAL, "scale must be finite and positive");
+  return SINK_ATTN_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SINK_ATTN_ELAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return SINK_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sink_attn_last_error(void) { return g_err; }
+
+int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                      const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                      const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                      const float* sinks, const int32_t* cu_seqlens, int32_t num_seqs,
+                      int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, float scale, int32_t causal,
+                      void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                      float* lse, void* stream) {
+  g_err[0] = '\0';
+  if (num_seqs < 0 || max_seqlen < 0) return fail(SINK_ATTN_EINVAL, "num_seqs and max_seqlen must be >= 0");
+  if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
+  if (int rc = check_scale(scale)) return rc;
+  if (causal != 0 && causal != 1) return fail(SINK_ATTN_EINVAL, "causal must be 0 or 1");
+  if (num_seqs == 0 || max_seqlen == 0) return SINK_ATTN_OK;
+  if (!q || !k || !v || !sinks || !cu_seqlens || !o) return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(SINK_ATTN_EINVAL, "q, k, v and o must be 16-byte aligned");
+  if (!aligned(sinks, 4) || !aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4)))
+    return fail(SINK_ATTN_EINVAL, "sinks, cu_seqlens and lse must be 4-byte aligned");
+  if (!stride_ok(q_stride_tok) || !stride_ok(q_stride_head) || !stride_ok(k_stride_tok) ||
+      !stride_ok(k_stride_head) || !stride_ok(v_stride_tok) || !stride_ok(v_stride_head) ||
+      !stride_ok(o_stride_tok) || !stride_ok(o_stride_head))
+    return fail(SINK_ATTN_EINVAL, "strides must be non-negative multiples of 8 elements");
+
+  const int group = num_q_heads / num_kv_heads;
+  const int hpw = sinkattn::prefill_heads_per_workgroup(group);
+  const int rows = sinkattn::prefill_rows_per_workgroup(group);
+  const int64_t n_qtiles = (max_seqlen + rows - 1) / rows;
+  const int64_t num_blocks = n_qtiles * num_seqs * (num_q_heads / hpw);
+  if (num_blocks > 0x7fffffff) return fail(SINK_ATTN_EUNSUPPORTED, "problem too large for one launch");
+
+  sinkattn::PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_st = q_stride_tok;
+  a.q_sh = q_stride_head;
+  a.k = static_cast<const uint16_t*>(k);
+  a.k_st = k_stride_tok;
+  a.k_sh = k_stride_head;
+  a.v = static_cast<const uint16_t*>(v);
+  a.v_st = v_stride_tok;
+  a.v_sh = v_stride_head;
+  a.sinks = sinks;
+  a.cu_seqlens = cu_seqlens;
+  a.o = static_cast<uint16_t*>(o);
+  a.o_st = o_stride_tok;
+  a.o_sh = o_stride_head;
+  a.lse = lse;
+  a.num_seqs = num_seqs;
+  a.n_qtiles = static_cast<int32_t>(n_qtiles);
+  a.num_q_heads = num_q_heads;
+  a.group = group;
+  a.head_groups = num_q_heads / hpw;
+  a.causal = causal;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launched(sinkattn::launch_prefill(a, head_dim, num_blocks, static_cast<hipStream_t>(stream)),
+                  "prefill");
+}
+
+int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_head,
+                           const void* k_cache, const void* v_cache, int64_t kv_stride_b,
+                           int64_t kv_stride_head, int64_t kv_stride_tok,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                           const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, float scale, int32_t split_size,
+                           int32_t num_splits, float* part_o, float* part_m,
+                           float* part_d, void* stream) {
+  g_err[0] = '\0';
+  if (batch < 0 || max_ctx < 0) return fail(SINK_ATTN_EINVAL, "batch and max_ctx must be >= 0");
+  if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
+  if (int rc = check_scale(scale)) return rc;
+  if (split_size <= 0 || split_size % 64 != 0)
+    return fail(SINK_ATTN_EINVAL, "split_size must be a positive multiple of 64 (got %d)", split_size);
+  if (num_splits <= 0) return fail(SINK_ATTN_EINVAL, "num_splits must be positive");
+  if (static_cast<int64_t>(num_splits) * split_size < max_ctx)
+    return fail(SINK_ATTN_EINVAL, "num_splits * split_size (%lld) does not cover max_ctx (%d)",
+                static_cast<long long>(num_splits) * split_size, max_ctx);
+  if (batch == 0) return SINK_ATTN_OK;
+  if (!q || !k_cache || !v_cache || !seq_lens || !sinks || !part_o || !part_m || !part_d)
+    return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(SINK_ATTN_EINVAL, "q, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(seq_lens, 4) || !aligned(sinks, 4) || !aligned(part_o, 4) || !aligned(part_m, 4) ||
+      !aligned(part_d, 4))
+    return fail(SINK_ATTN_EINVAL, "seq_lens, sinks and the partial buffers must be 4-byte aligned");
+  if (!stride_ok(q_stride_b) || !stride_ok(q_stride_head) || !stride_ok(kv_stride_b) ||
+      !stride_ok(kv_stride_head) || !stride_ok(kv_stride_tok))
+    return fail(SINK_ATTN_EINVAL, "strides must be non-negative multiples of 8 elements");
+
+  const int group = num_q_heads / num_kv_heads;
+  const int head_slices = (group + 15) / 16;
+  const int64_t num_blocks = static_cast<int64_t>(batch) * num_kv_heads * head_slices * num_splits;
+  if (num_blocks > 0x7fffffff) return fail(SINK_ATTN_EUNSUPPORTED, "problem too large for one launch");
+
+  sinkattn::DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_sb = q_stride_b;
+  a.q_sh = q_stride_head;
+  a.k_cache = static_cast<const uint16_t*>(k_cache);
+  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.kv_sb = kv_stride_b;
+  a.kv_sh = kv_stride_head;
+  a.kv_st = kv_stride_tok;
+  a.seq_lens = seq_lens;
+  a.sinks = sinks;
+  a.part_o = part_o;
+  a.part_m = part_m;
+  a.part_d = part_d;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.head_slices = head_slices;
+  a.split_size = split_size;
+  a.num_splits = num_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return launched(sinkattn::launch_decode_split(a, head_dim, num_blocks, static_cast<hipStream_t>(stream)),
+                  "decode_split");
+}
+
+int sink_attn_merge_states(const float* part_o, const float* part_m, const float* part_d,
+                           int32_t batch, int32_t num_q_heads, int32_t num_splits,
+                           int32_t head_dim, void* o, int64_t o_stride_b,
+                           int64_t o_stride_head, float* lse, void* stream) {
+  g_err[0] = '\0';
+  if (batch < 0) return fail(SINK_ATTN_EINVAL, "batch must be >= 0");
+  if (num_q_heads <= 0) return fail(SINK_ATTN_EINVAL, "num_q_heads must be positive");
+  if (num_splits <= 0) return fail(SINK_ATTN_EINVAL, "num_splits must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SINK_ATTN_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
+  if (batch == 0) return SINK_ATTN_OK;
+  if (!part_o || !part_m || !part_d || !o) return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  if (!aligned(o, 16)) return fail(SINK_ATTN_EINVAL, "o must be 16-byte aligned");
+  if (!aligned(part_o, 4) || !aligned(part_m, 4) || !aligned(part_d, 4) || (lse && !aligned(lse, 4)))
+    return fail(SINK_ATTN_EINVAL, "fp32 buffers must be 4-byte aligned");
+  if (!stride_ok(o_stride_b) || !stride_ok(o_stride_head))
+    return fail(SINK_ATTN_EINVAL, "strides must be non-negative multiples of 8 elements");
+  const int64_t rows = static_cast<int64_t>(batch) * num_q_heads;
+  if (rows > 0x7fffffff / 2) return fail(SINK_ATTN_EUNSUPPORTED, "problem too large for one launch");
+
+  sinkattn::MergeArgs a{};
+  a.part_o = part_o;
+  a.part_m = part_m;
+  a.part_d = part_d;
+  a.o = static_cast<uint16_t*>(o);
+  a.o_sb = o_stride_b;
+  a.o_sh = o_stride_head;
+  a.lse = lse;
+  a.rows = static_cast<int32_t>(rows);
+  a.num_q_heads = num_q_heads;
+  a.num_splits = num_splits;
+  return launched(sinkattn::launch_merge(a, head_dim, static_cast<hipStream_t>(stream)), "merge_states");
+}
+
+}  // extern "C"

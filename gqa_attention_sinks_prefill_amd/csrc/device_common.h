@@ -1,0 +1,82 @@
+// Device-side building blocks shared by the sink-attention kernels (gfx950).
+//
+// Register layouts of the two bf16 MFMA shapes used here (wave64):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds row l%32, k = 8*(l/32) .. +7   (8 bf16 = 16 bytes)
+//     B: lane l holds col l%32, k = 8*(l/32) .. +7
+//     D: lane l holds col l%32, rows 8*(i/4) + 4*(l/32) + i%4, i = 0..15
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] * B[32x16]
+//     A: lane l holds row l%16, k = 8*(l/16) .. +7
+//     B: lane l holds col l%16, k = 8*(l/16) .. +7
+//     D: lane l holds col l%16, rows 4*(l/16) + i, i = 0..3
+// The contraction index k may be permuted freely as long as A and B use the
+// same permutation; the kernels use that freedom to feed the softmax output
+// (in D layout) straight back as the B operand of the P.V product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Two floats -> two bf16 (round to nearest even), low half = lo.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions over the lane pair (l, l ^ 32).  permlane32_swap exchanges the
+// upper half of one register with the lower half of the other; with both
+// operands equal, every lane ends up holding its own value and its partner's.
+__device__ __forceinline__ float pair32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Same over (l, l ^ 16): permlane16_swap exchanges odd 16-lane rows of one
+// register with even rows of the other.
+__device__ __forceinline__ float pair16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// XOR swizzle of the 16-byte column chunk of a transposed-V LDS row.  Rows
+// d and d+1..d+7 land on distinct bank groups when read down a column, and
+// the eight rows 8c+e (c = 0..7, fixed e) written by one store instruction do
+// too.
+__device__ __forceinline__ int vt_swizzle(int d) { return (d ^ (d >> 3)) & 7; }
+
+}  // namespace sinkattn

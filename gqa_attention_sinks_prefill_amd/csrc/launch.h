@@ -1,0 +1,72 @@
+// Kernel argument blocks and launchers behind the C ABI (host + device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+struct PrefillArgs {
+  const uint16_t* q;
+  int64_t q_st, q_sh;
+  const uint16_t* k;
+  int64_t k_st, k_sh;
+  const uint16_t* v;
+  int64_t v_st, v_sh;
+  const float* sinks;
+  const int32_t* cu_seqlens;
+  uint16_t* o;
+  int64_t o_st, o_sh;
+  float* lse;             // [T, Hq] or null
+  int32_t num_seqs;
+  int32_t n_qtiles;       // ceil(max_seqlen / rows per workgroup)
+  int32_t num_q_heads;
+  int32_t group;          // query heads per KV head
+  int32_t head_groups;    // num_q_heads / heads per workgroup
+  int32_t causal;
+  float scale_log2;       // softmax scale * log2(e)
+};
+
+struct DecodeArgs {
+  const uint16_t* q;
+  int64_t q_sb, q_sh;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  int64_t kv_sb, kv_sh, kv_st;
+  const int32_t* seq_lens;
+  const float* sinks;
+  float* part_o;
+  float* part_m;
+  float* part_d;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;          // query heads per KV head
+  int32_t head_slices;    // ceil(group / 16): 16 query heads per workgroup
+  int32_t split_size;
+  int32_t num_splits;
+  float scale_log2;
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_m;
+  const float* part_d;
+  uint16_t* o;
+  int64_t o_sb, o_sh;
+  float* lse;
+  int32_t rows;           // batch * num_q_heads
+  int32_t num_q_heads;
+  int32_t num_splits;
+};
+
+// Workgroup shape of the prefill kernel for a given GQA group size.
+int prefill_heads_per_workgroup(int group);
+int prefill_rows_per_workgroup(int group);
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int64_t num_blocks,
+                          hipStream_t stream);
+hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,
+                               hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+
+}  // namespace sinkattn

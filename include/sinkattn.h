@@ -1,0 +1,153 @@
+/*
+ * sinkattn.h -- C ABI of the MI355X (gfx950) sink-attention library
+ * (libsinkattn.so): grouped-query attention whose softmax carries one learned
+ * logit per query head, for causal prefill and for split-KV decode.
+ *
+ * The operation.  "GPT-OSS on day 0" (Perplexity blog), section "Attention:
+ * GQA with attention sinks": each attention head owns a trained sink
+ * parameter that enters its softmax.  Section "Kernels for GPT-OSS /
+ * Sink-Attention": the sink is an extra bias term of the softmax next to the
+ * Q.K products; the softmax is computed online with the running maximum
+ * subtracted; the running maximum is seeded with the head's sink and the
+ * running scale with 1; and when the key range is split into chunks, only the
+ * first chunk carries the sink.  In formula form, for query row q of head h
+ * in GQA group g = h / (Hq/Hkv), over its visible keys J:
+ *
+ *     x_j = scale * q . k_j,   Z = exp(s_h) + sum_j exp(x_j),
+ *     o   = sum_j exp(x_j) / Z * v_j          (the sink has no value row)
+ *     lse = ln Z
+ *
+ * "Hosting Qwen on Blackwell" (Perplexity blog), section "Deployment on GB200
+ * NVL72": KV caches are stored in HND order, heads leading and the tokens of
+ * a head contiguous.  Every K/V argument below takes explicit strides, so HND
+ * (token stride D, head stride T*D) is the natural layout; d must always be
+ * the unit-stride dimension.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers.  bf16 tensors are passed as void* holding
+ *    IEEE bfloat16; sinks and partial states are fp32; lengths are int32.
+ *  - Strides are in ELEMENTS, must be multiples of 8 (16 bytes) and >= 0;
+ *    every bf16 pointer must be 16-byte aligned, fp32 pointers 4-byte aligned.
+ *  - The caller allocates and owns every buffer.  The library allocates
+ *    nothing, never synchronises, and enqueues all work on `stream` (a
+ *    hipStream_t; NULL is the null stream), so calls can be graph-captured.
+ *  - head_dim must be 64 or 128.  num_q_heads must be a multiple of
+ *    num_kv_heads; query head h uses KV head h / (num_q_heads/num_kv_heads).
+ *  - sinks[h] must be finite or -inf (-inf gives plain attention); +inf and
+ *    NaN are undefined.  Device-resident lengths are not checked (see each
+ *    function's preconditions); violating them is undefined behaviour.
+ *  - Return codes: SINK_ATTN_OK (0), SINK_ATTN_EINVAL (-1, bad argument,
+ *    nothing enqueued), SINK_ATTN_EUNSUPPORTED (-2, valid but not
+ *    implemented, nothing enqueued), SINK_ATTN_ELAUNCH (-3, the HIP launch
+ *    failed).  Every non-zero return sets a thread-local message readable
+ *    through sink_attn_last_error().  All argument checks run on the host
+ *    before any HIP call; no C++ exception crosses this boundary.
+ */
+#ifndef SINKATTN_H
+#define SINKATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SINK_ATTN_OK 0
+#define SINK_ATTN_EINVAL (-1)
+#define SINK_ATTN_EUNSUPPORTED (-2)
+#define SINK_ATTN_ELAUNCH (-3)
+
+/*
+ * Prefill over packed variable-length sequences ("Hosting Qwen on
+ * Blackwell", section "Prefillers": thousands of tokens of one request are
+ * processed at once, so prefill is compute-bound; "GPT-OSS on day 0",
+ * section "Kernels for GPT-OSS / Sink-Attention": the same sink-aware
+ * attention serves prefill and decode).
+ *
+ *   q   [T, Hq, D] bf16: token t, head h at q + t*q_stride_tok + h*q_stride_head.
+ *   k,v bf16: token t of KV head g at k + t*k_stride_tok + g*k_stride_head
+ *       (HND [Hkv, T, D]: k_stride_tok = D, k_stride_head = T*D).
+ *   sinks [Hq] fp32.
+ *   cu_seqlens [num_seqs + 1] int32, device: sequence s owns packed tokens
+ *       cu_seqlens[s] .. cu_seqlens[s+1]-1.  Precondition: cu_seqlens[0] = 0,
+ *       non-decreasing, every length <= max_seqlen.
+ *   max_seqlen: host-side upper bound of the sequence lengths (sizes the grid).
+ *   scale: softmax scale applied to q.k (1/sqrt(D) is usual); the sink is
+ *       not scaled.
+ *   causal: 1 = key j visible to query i iff j <= i (positions inside the
+ *       sequence); 0 = the whole sequence is visible.
+ *   o [T, Hq, D] bf16 (output, round-to-nearest-even) with its own strides.
+ *   lse: NULL, or fp32 [T, Hq] contiguous (output): ln Z of each row,
+ *       natural-log units, sink included.
+ * num_seqs = 0 or max_seqlen = 0 is a no-op.  o must not alias q, k or v.
+ */
+int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                      const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                      const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                      const float* sinks, const int32_t* cu_seqlens, int32_t num_seqs,
+                      int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, float scale, int32_t causal,
+                      void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                      float* lse, void* stream);
+
+/*
+ * First half of split-KV decode: one query token per request against its
+ * cached keys, with each request's key range cut into num_splits chunks of
+ * split_size tokens ("GPT-OSS on day 0", section "Kernels for GPT-OSS /
+ * Sink-Attention": attention is parallelised over heads and over the KV
+ * length, and only the first chunk carries the sink; "Hosting Qwen on
+ * Blackwell", section "Decoders": decode is memory-bound).
+ *
+ *   q [B, Hq, D] bf16: request b, head h at q + b*q_stride_b + h*q_stride_head.
+ *   k_cache, v_cache bf16, HND per request: token j of KV head g of request
+ *       b at base + b*kv_stride_b + g*kv_stride_head + j*kv_stride_tok (the
+ *       two caches share the strides).
+ *   seq_lens [B] int32, device.  Precondition: 0 <= seq_lens[b] <= max_ctx.
+ *   split_size: tokens per chunk, a positive multiple of 64.
+ *   num_splits: chunks per request; num_splits * split_size >= max_ctx.
+ *   Outputs, for row (b, h) and chunk c = 0 .. num_splits-1, chunk c covering
+ *   tokens [c*split_size, min((c+1)*split_size, seq_lens[b])):
+ *     part_o [B, Hq, num_splits, D] fp32: the chunk's output, already divided
+ *         by its own denominator;
+ *     part_m [B, Hq, num_splits] fp32: the chunk's running maximum (natural-
+ *         log units; chunk 0 includes the sink);
+ *     part_d [B, Hq, num_splits] fp32: the chunk's denominator relative to
+ *         exp(part_m) (chunk 0 includes the sink term).
+ *   An empty chunk without the sink is written as (o, m, d) = (0, -inf, 0).
+ * Feed the partials to sink_attn_merge_states on the same stream.
+ */
+int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_head,
+                           const void* k_cache, const void* v_cache, int64_t kv_stride_b,
+                           int64_t kv_stride_head, int64_t kv_stride_tok,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                           const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, float scale, int32_t split_size,
+                           int32_t num_splits, float* part_o, float* part_m,
+                           float* part_d, void* stream);
+
+/*
+ * Second half of split-KV decode: merge each row's chunk states by their
+ * log-sum-exp weights (the pages state that chunks are formed and that only
+ * the first carries the sink; the merge is the exact recombination this
+ * implies):  M = max_c m_c,  w_c = d_c * exp(m_c - M),
+ *            o = sum_c w_c o_c / sum_c w_c,  lse = M + ln sum_c w_c.
+ * Chunks with m_c = -inf get weight 0; a row with no weight gives o = 0 and
+ * lse = -inf.
+ *   part_o, part_m, part_d: as written by sink_attn_decode_split.
+ *   o [B, Hq, D] bf16 (output): row (b, h) at o + b*o_stride_b + h*o_stride_head.
+ *   lse: NULL, or fp32 [B, Hq] contiguous (output).
+ */
+int sink_attn_merge_states(const float* part_o, const float* part_m, const float* part_d,
+                           int32_t batch, int32_t num_q_heads, int32_t num_splits,
+                           int32_t head_dim, void* o, int64_t o_stride_b,
+                           int64_t o_stride_head, float* lse, void* stream);
+
+/* Message of the last failed call on this thread ("" if none).  The pointer
+ * stays valid until the next call into the library on the same thread. */
+const char* sink_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKATTN_H */

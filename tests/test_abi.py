@@ -1,0 +1,152 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol that
+include/sinkattn.h declares, and rejects bad arguments on the host before any
+HIP call (so these run without a GPU; no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gqa_attention_sinks_prefill_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sa.library_path()),
+                                reason="libsinkattn.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sink_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_exported_api():
+    assert declared_functions() == sorted(sa.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def _prefill(**kw):
+    args = dict(q=16, q_st=512, q_sh=64, k=16, k_st=64, k_sh=64 * 256, v=16, v_st=64,
+                v_sh=64 * 256, sinks=4, cu=4, num_seqs=1, max_seqlen=256, hq=8, hkv=2, d=64,
+                scale=0.125, causal=1, o=16, o_st=512, o_sh=64, lse=None)
+    args.update(kw)
+    a = args
+    lib = sa.load_library()
+    rc = lib.sink_attn_prefill(a["q"], a["q_st"], a["q_sh"], a["k"], a["k_st"], a["k_sh"],
+                               a["v"], a["v_st"], a["v_sh"], a["sinks"], a["cu"], a["num_seqs"],
+                               a["max_seqlen"], a["hq"], a["hkv"], a["d"], a["scale"],
+                               a["causal"], a["o"], a["o_st"], a["o_sh"], a["lse"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+# Fake, never-dereferenced "device" addresses: every case below must fail in
+# validation, before anything touches them.
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(q=None), -1, "null"),
+    (dict(o=None), -1, "null"),
+    (dict(cu=None), -1, "null"),
+    (dict(hq=6, hkv=4), -1, "multiple"),
+    (dict(hkv=0), -1, "positive"),
+    (dict(d=96), -2, "head_dim"),
+    (dict(d=256), -2, "head_dim"),
+    (dict(q=24), -1, "aligned"),
+    (dict(sinks=6), -1, "aligned"),
+    (dict(k_st=60), -1, "multiples of 8"),
+    (dict(o_sh=-8), -1, "multiples of 8"),
+    (dict(num_seqs=-1), -1, ">= 0"),
+    (dict(causal=2), -1, "causal"),
+    (dict(scale=0.0), -1, "scale"),
+    (dict(scale=float("nan")), -1, "scale"),
+])
+def test_prefill_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _prefill(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_prefill_empty_work_is_a_noop():
+    assert _prefill(num_seqs=0, q=None, o=None)[0] == 0
+    assert _prefill(max_seqlen=0)[0] == 0
+
+
+def _decode(**kw):
+    a = dict(q=16, q_sb=4096, q_sh=64, k=16, v=16, kv_sb=8 * 1024 * 64, kv_sh=1024 * 64,
+             kv_st=64, lens=4, batch=4, max_ctx=1024, sinks=4, hq=64, hkv=8, d=64,
+             scale=0.125, split=256, nsplit=4, po=4, pm=4, pd=4)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_decode_split(a["q"], a["q_sb"], a["q_sh"], a["k"], a["v"], a["kv_sb"],
+                                    a["kv_sh"], a["kv_st"], a["lens"], a["batch"], a["max_ctx"],
+                                    a["sinks"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                    a["split"], a["nsplit"], a["po"], a["pm"], a["pd"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(k=None), -1, "null"),
+    (dict(pd=None), -1, "null"),
+    (dict(split=100), -1, "split_size"),
+    (dict(split=0), -1, "split_size"),
+    (dict(nsplit=3), -1, "cover"),
+    (dict(nsplit=0), -1, "num_splits"),
+    (dict(hq=12), -1, "multiple"),
+    (dict(d=80), -2, "head_dim"),
+    (dict(v=8), -1, "aligned"),
+    (dict(kv_st=66), -1, "multiples of 8"),
+    (dict(batch=-2), -1, ">= 0"),
+])
+def test_decode_split_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _decode(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_decode_split_empty_batch_is_a_noop():
+    assert _decode(batch=0, q=None)[0] == 0
+
+
+def _merge(**kw):
+    a = dict(po=4, pm=4, pd=4, batch=2, hq=8, ns=4, d=64, o=16, o_sb=512, o_sh=64, lse=None)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_merge_states(a["po"], a["pm"], a["pd"], a["batch"], a["hq"], a["ns"],
+                                    a["d"], a["o"], a["o_sb"], a["o_sh"], a["lse"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(po=None), -1, "null"),
+    (dict(o=None), -1, "null"),
+    (dict(ns=0), -1, "num_splits"),
+    (dict(hq=0), -1, "num_q_heads"),
+    (dict(d=32), -2, "head_dim"),
+    (dict(o=18), -1, "aligned"),
+    (dict(lse=6), -1, "aligned"),
+    (dict(o_sh=3), -1, "multiples of 8"),
+])
+def test_merge_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _merge(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_error_message_clears_on_success():
+    _merge(po=None)
+    assert sa.load_library().sink_attn_last_error() != b""
+    assert _merge(batch=0)[0] == 0
+    assert sa.load_library().sink_attn_last_error() == b""
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        sa.sink_attn_prefill(q, q, q, torch.zeros(2), torch.zeros(2, dtype=torch.int32), 4)

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Bar: max-abs <= 2e-2 and mean-abs <= 2e-3 over the compared output elements
+(bf16 inputs, fp32 accumulation).  Every output buffer is pre-filled with NaN,
+so an element the kernels fail to write fails the test.  Full-size workloads
+are checked on sampled rows (each computed one by one by the oracle) plus
+properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_attention_sinks_prefill_amd as sa
+import oracle
+from gqa_attention_sinks_prefill_amd import workloads as wl
+from parity_utils import (assert_close, assert_lse_close, gather_rows, sample_prefill_rows)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda:0"
+
+
+def _prefill_gpu(inp, *, causal=True, kv_layout="hnd", with_lse=True):
+    q = inp["q"].to(DEV)
+    k, v = inp["k"].to(DEV), inp["v"].to(DEV)
+    if kv_layout == "nhd":
+        k, v = k.transpose(0, 1).contiguous(), v.transpose(0, 1).contiguous()
+    T, Hq, D = q.shape
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((T, Hq), float("nan"), dtype=torch.float32, device=DEV) if with_lse else None
+    sa.sink_attn_prefill(q, k, v, inp["sinks"].to(DEV), inp["cu_seqlens"].to(DEV),
+                         inp["max_seqlen"], causal=causal, kv_layout=kv_layout, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _prefill_case(lens, Hq, Hkv, D, seed, sink_range=(-4.0, 4.0), edges=None):
+    cfg = wl.PrefillConfig("case", tuple(lens), len(lens), None, Hq, Hkv, D, sink_range,
+                           seed=seed, edge_sinks=edges or {})
+    return wl.prefill_inputs(cfg)
+
+
+# ------------------------------------------------------------------ prefill --
+def test_prefill_tiny_all_rows():
+    inp = wl.prefill_inputs(wl.TINY_PREFILL)
+    out, lse = _prefill_gpu(inp)
+    o_ref, lse_ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                       inp["cu_seqlens"], causal=True, scale=wl.TINY_PREFILL.scale)
+    assert_close(out.reshape(-1, 64), o_ref, what="tiny prefill O")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="tiny prefill lse")
+
+
+def test_prefill_tiny_is_deterministic():
+    inp = wl.prefill_inputs(wl.TINY_PREFILL)
+    a, la = _prefill_gpu(inp)
+    b, lb = _prefill_gpu(inp)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+
+
+def test_prefill_gptoss_shape_sampled_rows():
+    cfg = wl.GPTOSS_PREFILL
+    inp = wl.prefill_inputs(cfg)
+    out, lse = _prefill_gpu(inp)
+    assert not torch.isnan(out).any().item(), "unwritten or non-finite outputs"
+    rows = sample_prefill_rows(inp["cu_seqlens"], cfg.num_q_heads, n_random=600, seed=1)
+    o_ref, lse_ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                       inp["cu_seqlens"], causal=True, scale=cfg.scale, rows=rows)
+    assert_close(gather_rows(out, rows), o_ref, what="gpt-oss prefill O (sampled rows)")
+    idx = torch.tensor(rows)
+    assert_lse_close(lse.cpu()[idx[:, 0], idx[:, 1]], lse_ref, what="gpt-oss prefill lse")
+    # any size: each output is a sub-convex combination of V rows
+    assert out.abs().max().item() <= inp["v"].abs().max().item() + 1e-2
+
+
+def test_prefill_varlen_wide_gqa_d128_sampled_rows():
+    cfg = wl.VARLEN_PREFILL
+    inp = wl.prefill_inputs(cfg)
+    out, lse = _prefill_gpu(inp)
+    assert not torch.isnan(out).any().item(), "unwritten or non-finite outputs"
+    rows = sample_prefill_rows(inp["cu_seqlens"], cfg.num_q_heads, n_random=400, seed=4)
+    cu = [int(x) for x in inp["cu_seqlens"]]
+    rows += [(cu[s] + p, 5) for s in range(len(cu) - 1) for p in (0, 7, cu[s + 1] - cu[s] - 1)]
+    rows = sorted(set(rows))
+    o_ref, lse_ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                       inp["cu_seqlens"], causal=True, scale=cfg.scale, rows=rows)
+    assert_close(gather_rows(out, rows), o_ref, what="varlen d128 prefill O (sampled rows)")
+    idx = torch.tensor(rows)
+    assert_lse_close(lse.cpu()[idx[:, 0], idx[:, 1]], lse_ref, what="varlen d128 prefill lse")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 1), (8, 8), (4, 2), (32, 1)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_ragged_edges_all_rows(Hq, Hkv, D, causal):
+    """Lengths around tile edges, a zero-length sequence, GQA groups of 1, 2, 4, 32."""
+    lens = [1, 31, 33, 0, 64, 65, 127, 200]
+    inp = _prefill_case(lens, Hq, Hkv, D, seed=100 + Hq + D + causal,
+                        edges={0: float("-inf"), Hq - 1: 20.0})
+    out, lse = _prefill_gpu(inp, causal=causal)
+    o_ref, lse_ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                       inp["cu_seqlens"], causal=causal, scale=1 / math.sqrt(D))
+    assert_close(out.reshape(-1, D), o_ref, what=f"ragged prefill Hq={Hq} Hkv={Hkv} D={D}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="ragged prefill lse")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_nhd_kv_layout(D):
+    inp = _prefill_case([150, 77], 8, 2, D, seed=7)
+    out, _ = _prefill_gpu(inp, kv_layout="nhd", with_lse=False)
+    o_ref, _, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["cu_seqlens"],
+                                 causal=True, scale=1 / math.sqrt(D))
+    assert_close(out.reshape(-1, D), o_ref, what="nhd prefill O")
+
+
+def test_prefill_empty_batches_leave_outputs_untouched():
+    inp = _prefill_case([0, 0], 4, 1, 64, seed=3)
+    q = torch.zeros(1, 4, 64, dtype=torch.bfloat16, device=DEV)
+    out = torch.full_like(q, 7.0)
+    sa.sink_attn_prefill(q, q[:, :1].transpose(0, 1), q[:, :1].transpose(0, 1),
+                         inp["sinks"].to(DEV), inp["cu_seqlens"].to(DEV), 0, out=out)
+    cu0 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sa.sink_attn_prefill(q, q[:, :1].transpose(0, 1), q[:, :1].transpose(0, 1),
+                         inp["sinks"].to(DEV), cu0, 16, out=out)
+    # a real launch whose every workgroup finds an empty sequence
+    sa.sink_attn_prefill(q, q[:, :1].transpose(0, 1), q[:, :1].transpose(0, 1),
+                         inp["sinks"].to(DEV), inp["cu_seqlens"].to(DEV), 16, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+# ------------------------------------------------------------------- decode --
+def _decode_gpu(inp, split_size, num_splits=None, *, max_ctx=None):
+    q = inp["q"].to(DEV)
+    kc, vc = inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    B, Hq, D = q.shape
+    max_ctx = kc.shape[2] if max_ctx is None else max_ctx
+    ns = -(-max_ctx // split_size) if num_splits is None else num_splits
+    po = torch.full((B, Hq, ns, D), float("nan"), device=DEV)
+    pm = torch.full((B, Hq, ns), float("nan"), device=DEV)
+    pd = torch.full((B, Hq, ns), float("nan"), device=DEV)
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, Hq), float("nan"), device=DEV)
+    lens, sinks = inp["seq_lens"].to(DEV), inp["sinks"].to(DEV)
+    sa.sink_attn_decode_split(q, kc, vc, lens, sinks, split_size, ns, max_ctx=max_ctx,
+                              part_o=po, part_m=pm, part_d=pd)
+    sa.sink_attn_merge_states(po, pm, pd, out=out, lse=lse)
+    torch.cuda.synchronize()
+    del kc, vc
+    return out, lse, (po, pm, pd)
+
+
+def _check_decode(inp, out, lse, what):
+    o_ref, lse_ref, _ = oracle.decode(inp["q"], inp["k_cache"], inp["v_cache"],
+                                      inp["seq_lens"], inp["sinks"])
+    D = inp["q"].shape[-1]
+    assert_close(out.reshape(-1, D), o_ref, what=f"{what} O")
+    assert_lse_close(lse.reshape(-1), lse_ref, what=f"{what} lse")
+
+
+def test_decode_split_kv_full_config():
+    cfg = wl.SPLIT_DECODE
+    inp = wl.decode_inputs(cfg)
+    out, lse, (po, pm, pd) = _decode_gpu(inp, cfg.split_size)
+    _check_decode(inp, out, lse, "split decode")
+    # chunk states against the oracle's own chunk states on sampled rows
+    rng = np.random.default_rng(2)
+    rows = sorted({(int(rng.integers(cfg.batch)), int(rng.integers(cfg.num_q_heads)))
+                   for _ in range(64)} | {(0, 0), (cfg.batch - 1, cfg.num_q_heads - 1)})
+    o_c, m_c, d_c = oracle.chunk_states(inp["q"], inp["k_cache"], inp["v_cache"],
+                                        inp["seq_lens"], inp["sinks"], cfg.split_size,
+                                        cfg.num_splits, rows=rows)
+    idx = torch.tensor(rows)
+    g_o = po.cpu()[idx[:, 0], idx[:, 1]]
+    g_m = pm.cpu()[idx[:, 0], idx[:, 1]].double().numpy()
+    g_d = pd.cpu()[idx[:, 0], idx[:, 1]].double().numpy()
+    assert_close(g_o, o_c, what="split decode chunk o")
+    np.testing.assert_allclose(g_m, m_c, rtol=0, atol=2e-3)
+    np.testing.assert_allclose(g_d, d_c, rtol=2e-3)
+
+
+def test_decode_is_deterministic():
+    cfg = wl.DecodeConfig("det", 8, None, (1, 5000), 5000, 64, 8, 64, (-4.0, 4.0),
+                          split_size=1024, seed=5)
+    inp = wl.decode_inputs(cfg)
+    a, la, _ = _decode_gpu(inp, 1024)
+    b, lb, _ = _decode_gpu(inp, 1024)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+
+
+@pytest.mark.parametrize("batch", wl.RAGGED_BATCHES)
+def test_decode_ragged_long_context(batch):
+    cfg = wl.ragged_decode(batch)
+    inp = wl.decode_inputs(cfg)     # slots past each length hold NaN
+    out, lse, _ = _decode_gpu(inp, cfg.split_size)
+    _check_decode(inp, out, lse, f"ragged decode B={batch}")
+    # head 0 (sink -inf) is plain attention: sink share 0; head 63 (sink +20)
+    # is dominated by the sink: its output is tiny.
+    assert out[:, 63].abs().max().item() < 5e-3
+
+
+@pytest.mark.parametrize("split", [64, 256, 1024, 4096])
+def test_decode_split_size_invariance(split):
+    cfg = wl.DecodeConfig("splits", 6, None, (1, 3000), 3000, 16, 2, 64, (-4.0, 4.0),
+                          split_size=split, seed=9, edge_sinks={1: float("-inf"), 2: 20.0})
+    inp = wl.decode_inputs(cfg)
+    out, lse, _ = _decode_gpu(inp, split, -(-3000 // split) + 2)     # + 2 empty chunks
+    _check_decode(inp, out, lse, f"split {split}")
+
+
+def test_decode_edge_lengths():
+    lens = [0, 1, 63, 64, 65, 255, 256, 257, 1024, 1025, 0]
+    B, Hq, Hkv, D, max_ctx = len(lens), 8, 2, 64, 1280
+    g = torch.Generator().manual_seed(31)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    kc = torch.full((B, Hkv, max_ctx, D), float("nan"), dtype=torch.bfloat16)
+    vc = torch.full((B, Hkv, max_ctx, D), float("nan"), dtype=torch.bfloat16)
+    for b, L in enumerate(lens):
+        kc[b, :, :L] = torch.randn(Hkv, L, D, generator=g).to(torch.bfloat16)
+        vc[b, :, :L] = torch.randn(Hkv, L, D, generator=g).to(torch.bfloat16)
+    sinks = torch.tensor([float("-inf"), 0.0, 1.0, -2.0, 20.0, float("-inf"), 3.0, -4.0])
+    inp = dict(q=q, k_cache=kc, v_cache=vc, seq_lens=torch.tensor(lens, dtype=torch.int32),
+               sinks=sinks)
+    out, lse, _ = _decode_gpu(inp, 256)
+    _check_decode(inp, out, lse, "edge lengths")
+    assert torch.all(out[0] == 0) and torch.all(out[-1] == 0)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(64, 2, 128), (8, 8, 128), (32, 1, 64)])
+def test_decode_head_dims_and_groups(Hq, Hkv, D):
+    cfg = wl.DecodeConfig("groups", 5, None, (1, 2500), 2500, Hq, Hkv, D, (-4.0, 4.0),
+                          split_size=512, seed=Hq + D, edge_sinks={0: float("-inf")})
+    inp = wl.decode_inputs(cfg)
+    out, lse, _ = _decode_gpu(inp, 512)
+    _check_decode(inp, out, lse, f"decode Hq={Hq} Hkv={Hkv} D={D}")
+
+
+def test_decode_strided_query_and_output():
+    """Non-contiguous q / out views with head stride != D."""
+    cfg = wl.DecodeConfig("strided", 3, None, (100, 900), 1024, 8, 2, 64, (-4.0, 4.0),
+                          split_size=256, seed=12)
+    inp = wl.decode_inputs(cfg)
+    qbig = torch.zeros(3, 8, 128, dtype=torch.bfloat16)
+    qbig[:, :, 32:96] = inp["q"]
+    q = qbig.to(DEV)[:, :, 32:96]
+    kc, vc = inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    po, pm, pd = sa.sink_attn_decode_split(q, kc, vc, inp["seq_lens"].to(DEV),
+                                           inp["sinks"].to(DEV), 256)
+    obig = torch.full((3, 8, 192), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = obig[:, :, 64:128]
+    sa.sink_attn_merge_states(po, pm, pd, out=out)
+    torch.cuda.synchronize()
+    o_ref, _, _ = oracle.decode(inp["q"], inp["k_cache"], inp["v_cache"], inp["seq_lens"],
+                                inp["sinks"])
+    assert_close(out.reshape(-1, 64), o_ref, what="strided decode O")
+    assert torch.isnan(obig[:, :, :64]).all() and torch.isnan(obig[:, :, 128:]).all()
