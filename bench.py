@@ -69,36 +69,82 @@ def measured_traffic(kernel: str):
 
 
 def cpu_baseline(pre_inp, cfg, out_gpu, seconds: float, seed: int = 0):
-    """Time the fp64 oracle on random prefill rows for about `seconds`, and use
-    the same rows as a parity spot check of the timed GPU output."""
+    """Time the fp64 oracle on the prefill workload's rows, in a seeded random
+    order and in chunks, until every row is done or `seconds` have passed; the
+    same rows are the parity check of the timed GPU output."""
     import oracle   # test infrastructure: only this leg of the benchmark uses it
 
     threads = oracle.default_threads()
-    rng = np.random.default_rng(seed)
     T, Hq, D = pre_inp["q"].shape
-    done_rows, flops, elapsed = [], 0.0, 0.0
-    outs = []
-    batch = 256
-    while elapsed < seconds:
-        rows = np.stack([rng.integers(0, T, batch), rng.integers(0, Hq, batch)], 1)
+    order = np.random.default_rng(seed).permutation(T * Hq)
+    rows_all = np.stack([order // Hq, order % Hq], 1)
+    chunk = 16384
+    flops, elapsed, done = 0.0, 0.0, 0
+    max_err, sum_err = 0.0, 0.0
+    out_cpu = out_gpu.detach().cpu()
+    while done < len(rows_all) and elapsed < seconds:
+        rows = rows_all[done:done + chunk]
         t0 = time.perf_counter()
         o, _, _ = oracle.prefill(pre_inp["q"], pre_inp["k"], pre_inp["v"], pre_inp["sinks"],
                                  pre_inp["cu_seqlens"], causal=True, scale=cfg.scale,
                                  rows=rows, threads=threads)
         elapsed += time.perf_counter() - t0
         flops += float(np.sum(4.0 * D * (rows[:, 0] + 1)))      # one sequence: pos = token
-        done_rows.append(rows)
-        outs.append(o)
-    rows = np.concatenate(done_rows)
-    ref = np.concatenate(outs)
-    got = out_gpu.detach().cpu()[torch.from_numpy(rows[:, 0]), torch.from_numpy(rows[:, 1])]
-    err = np.abs(got.double().numpy() - ref)
+        got = out_cpu[torch.from_numpy(rows[:, 0]), torch.from_numpy(rows[:, 1])]
+        err = np.abs(got.double().numpy() - o)
+        max_err = max(max_err, float(err.max()))
+        sum_err += float(err.sum())
+        done += len(rows)
+    full = done == len(rows_all)
+    what = ("all" if full else f"{done} random") + f" of the {len(rows_all)} (token, head) rows"
     return ({"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
              "kind": "oracle",
-             "sample": f"{len(rows)} random (token, head) rows of the 8192-token prefill, "
-                       f"{flops:.3g} algorithmic flop in {elapsed:.1f} s, fp64 C + OpenMP"},
-            {"rows": int(len(rows)), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
-             "bound_max_abs": 2e-2, "bound_mean_abs": 2e-3})
+             "sample": f"{what} of the 8192-token GPT-OSS-shaped prefill, {flops:.3g} "
+                       f"algorithmic flop in {elapsed:.1f} s, fp64 C + OpenMP"},
+            {"rows": int(done), "all_rows": bool(full), "max_abs": max_err,
+             "mean_abs": sum_err / (done * D), "bound_max_abs": 2e-2, "bound_mean_abs": 2e-3})
+
+
+def varlen_prefill_measurement(dev, stream, reps: int):
+    """TFLOP/s of the wide-GQA varlen prefill (16 packed sequences of U[512, 6000]
+    tokens, 64 q / 4 KV heads, head_dim 128, causal), event-timed like the main line."""
+    cfg = wl.VARLEN_PREFILL
+    inp = wl.prefill_inputs(cfg)
+    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+    sinks, cu = inp["sinks"].to(dev), inp["cu_seqlens"].to(dev)
+    out = torch.empty_like(q)
+    run = lambda: sa.sink_attn_prefill(q, k, v, sinks, cu, inp["max_seqlen"], causal=True,
+                                       scale=cfg.scale, out=out, stream=stream)
+    run()
+    run()
+    torch.cuda.synchronize()
+    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+         for _ in range(reps)]
+    for a, b in e:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
+    flops = wl.prefill_flops(inp["seqlens"].tolist(), cfg.num_q_heads, cfg.head_dim)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": cfg.name, "value": round(tf, 2), "unit": "TFLOP/s",
+            "mean_launch_ms": round(ms, 4), "algorithmic_flop_per_launch": flops,
+            "roofline": {"bound": "mfma", "peak": round(PEAK_BF16_TFLOPS, 1),
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
+def copy_calibration(dev, reps: int):
+    """A plain device-to-device copy of 1 GiB: reads and writes exactly 2^30
+    bytes each, the reference that scales the HBM byte counters."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(max(1, reps)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "reps": max(1, reps)}), flush=True)
 
 
 def main():
@@ -106,8 +152,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+    ap.add_argument("--cpu-seconds", type=float, default=45.0,
                     help="host time budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
+                    help="launch only one part of the step (for hardware-counter runs)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra wide-GQA varlen (head_dim 128) prefill measurement")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy instead (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -119,18 +171,23 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    if args.copy_calibration:
+        copy_calibration(dev, args.steps)
+        return
 
     # ---- inputs, resident in HBM before timing ---------------------------------
     pcfg, dcfg = wl.GPTOSS_PREFILL, wl.SPLIT_DECODE
-    pre = wl.prefill_inputs(pcfg)
-    dec = wl.decode_inputs(dcfg)
+    run_p, run_d = args.only in ("all", "prefill"), args.only in ("all", "decode")
+    pre = wl.prefill_inputs(pcfg) if run_p else wl.prefill_inputs(wl.TINY_PREFILL)
+    dec = wl.decode_inputs(dcfg) if run_d else wl.decode_inputs(
+        wl.DecodeConfig("unused", 1, 64, None, 64, 64, 8, 64, (-4.0, 4.0), 64, 0))
     q, k, v = pre["q"].to(dev), pre["k"].to(dev), pre["v"].to(dev)
     sinks_p, cu = pre["sinks"].to(dev), pre["cu_seqlens"].to(dev)
     out = torch.empty_like(q)
     dq, kc, vc = dec["q"].to(dev), dec["k_cache"].to(dev), dec["v_cache"].to(dev)
     lens, sinks_d = dec["seq_lens"].to(dev), dec["sinks"].to(dev)
     B, Hq, D = dq.shape
-    ns = dcfg.num_splits
+    ns = -(-kc.shape[2] // dcfg.split_size)
     po = torch.empty(B, Hq, ns, D, device=dev)
     pm = torch.empty(B, Hq, ns, device=dev)
     pd = torch.empty(B, Hq, ns, device=dev)
@@ -142,14 +199,17 @@ def main():
 
     def step(e=None):
         if e: e[0].record(stream)
-        sa.sink_attn_prefill(q, k, v, sinks_p, cu, pre["max_seqlen"], causal=True,
-                             scale=pcfg.scale, out=out, stream=stream)
+        if run_p:
+            sa.sink_attn_prefill(q, k, v, sinks_p, cu, pre["max_seqlen"], causal=True,
+                                 scale=pcfg.scale, out=out, stream=stream)
         if e: e[1].record(stream)
-        sa.sink_attn_decode_split(dq, kc, vc, lens, sinks_d, dcfg.split_size, ns,
-                                  scale=dcfg.scale, part_o=po, part_m=pm, part_d=pd,
-                                  stream=stream)
+        if run_d:
+            sa.sink_attn_decode_split(dq, kc, vc, lens, sinks_d, dcfg.split_size, ns,
+                                      scale=dcfg.scale, part_o=po, part_m=pm, part_d=pd,
+                                      stream=stream)
         if e: e[2].record(stream)
-        sa.sink_attn_merge_states(po, pm, pd, out=dout, stream=stream)
+        if run_d:
+            sa.sink_attn_merge_states(po, pm, pd, out=dout, stream=stream)
         if e: e[3].record(stream)
 
     for _ in range(args.warmup):
@@ -206,7 +266,11 @@ def main():
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
     }
-    if args.cpu_seconds > 0:
+    if run_p and not args.no_extra:
+        res["extra"] = [varlen_prefill_measurement(dev, stream, max(3, args.steps // 2))]
+    if args.only != "all":
+        res["note"] = f"--only {args.only}: the other part of the step was not launched"
+    if args.cpu_seconds > 0 and run_p:
         cb, parity = cpu_baseline(pre, pcfg, out, args.cpu_seconds)
         res["cpu_baseline"] = cb
         res["parity_spot_check"] = parity

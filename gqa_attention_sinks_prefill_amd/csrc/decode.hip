@@ -10,17 +10,21 @@
 //
 // decode_split_kernel: one workgroup (4 waves) per (request b, KV head g,
 // 16-head slice of g's query heads, chunk c).  The K/V of the chunk are read
-// exactly once and serve every query head of the group.  Each wave takes 64
-// consecutive keys per step; the 4 waves cover 256 keys per step.
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d loaded
-//     straight from HBM (16 bytes per lane, whole 128-byte rows per 8 lanes),
-//     B = Q^T of up to 16 heads (padding columns are zero).
-//   * the softmax state is per lane (column = head); row max / sum reduce over
-//     the four 16-lane rows with permlane16/32 swaps.
-//   * O^T += V^T P^T on the same MFMA; V goes through a per-wave LDS tile
-//     written transposed, P^T comes straight from the S^T accumulators.
-//   * at the end the 4 waves' states are merged through LDS and the chunk's
-//     (o / d, m, d) is written in fp32.  Only wave 0 of chunk 0 seeds the sink.
+// exactly once and serve every query head of the group.  The chunk is cut
+// into 64-key sub-tiles; wave w takes sub-tiles w, w+4, w+8, ... and runs its
+// own pipeline with no workgroup barrier until the final merge:
+//   * K of the next sub-tile is loaded HBM -> registers and V of the next
+//     sub-tile is copied HBM -> LDS (buffer->LDS DMA into the wave's double
+//     buffer) while the current sub-tile is computed; both streams are read
+//     once, so they are loaded non-temporally;
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d straight
+//     from the registers, B = Q^T of up to 16 heads (padding columns zero);
+//   * the softmax state is per lane (column = head); row max and sum reduce
+//     over the four 16-lane rows with permlane16/32 swaps;
+//   * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T
+//     accumulators, V^T from the row-major V tile via the transposing LDS read.
+// At the end the 4 waves' states are merged through LDS and the chunk's
+// (o / d, m, d) is written in fp32.  Only wave 0 of chunk 0 seeds the sink.
 // merge_kernel: one wave per (b, h) row, lane = d; log-sum-exp weighted sum of
 // the chunk states, rounded to bf16.
 #include "device_common.h"
@@ -31,22 +35,20 @@ namespace sinkattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaveKeys = 64;                 // keys per wave per step
-constexpr int kStepKeys = 4 * kWaveKeys;      // keys per workgroup per step
+constexpr int kSub = 64;                      // keys per sub-tile
 
-// Position of key k (0..63) in a transposed-V row: within each 32-key half,
-// the 8 keys one 16x16x32 MFMA lane row-group b consumes
-// ({4b..4b+3, 16+4b..16+4b+3}) are made contiguous.
-__device__ __forceinline__ int vt_pos16(int k) {
-  return (k & 32) + (((k >> 2) & 3) << 3) + (((k >> 4) & 1) << 2) + (k & 3);
-}
+// Chunk swizzle of the row-major V sub-tile: a transposing read covers four
+// consecutive rows x two adjacent 16-byte chunks per 16-lane group, and XOR
+// with 2 * (row % 4) puts those eight chunk reads in eight bank groups.
+__device__ __forceinline__ int dv_swz(int row) { return 2 * (row & 3); }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-  constexpr int DC = D / 8;                                // 16-byte chunks per row
-  constexpr int VIT = (kWaveKeys / 2) * DC / 64;           // V items per lane
-  constexpr int VT = D * kWaveKeys;                        // elements of one wave's V^T tile
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * VT];
+  constexpr int DC = D / 8;                  // 16-byte chunks per row
+  constexpr int TILE = kSub * D;             // elements of one V sub-tile
+  constexpr int NDMA = kSub * DC / 64;       // DMA instructions per V sub-tile
+  constexpr int NCC = D / 32;                // 32-d chunks of a K fragment row
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * 2 * TILE];
 
   int unit = blockIdx.x;
   const int c = unit % a.num_splits;
@@ -68,16 +70,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
   const int len = a.seq_lens[b];
   const int lo = c * a.split_size;
-  const int hi = min(lo + a.split_size, len);
-  const int n = max(hi - lo, 0);
-  const int nsteps = (n + kStepKeys - 1) / kStepKeys;
+  const int n = max(min(a.split_size, len - lo), 0);    // keys of this chunk
+  const int n_sub = (n + kSub - 1) / kSub;
 
   // Q^T fragments: column = head, k = d
-  u32x4_t qf[D / 32];
+  u32x4_t qf[NCC];
   {
     const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + 8 * lgrp;
 #pragma unroll
-    for (int cc = 0; cc < D / 32; ++cc) {
+    for (int cc = 0; cc < NCC; ++cc) {
       u32x4_t t = load16(qp + 32 * cc);
       qf[cc] = hvalid ? t : u32x4_t{0, 0, 0, 0};
     }
@@ -86,106 +87,95 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   // state: the sink seeds wave 0 of chunk 0 only, counted once (row group 0)
   const float sink = hvalid ? a.sinks[h] : -INFINITY;
   const bool seeded = (c == 0) && (wave == 0);
-  float m = seeded ? sink * kLog2e : -INFINITY;
+  float m = seeded ? fmaxf(sink * kLog2e, -__FLT_MAX__) : -__FLT_MAX__;
   float l = (seeded && lgrp == 0 && sink != -INFINITY) ? 1.f : 0.f;
   f32x4_t acc[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) acc[db] = f32x4_t{};
 
-  const uint16_t* kbase = a.k_cache + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
-  const uint16_t* vbase = a.v_cache + (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
-  uint16_t* vt = smem + wave * VT;
+  // K / V of this chunk through buffer resources (loads past its end read 0)
+  const int st2 = (int)(a.kv_st * 2);
+  const int64_t base = (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh + (int64_t)lo * a.kv_st;
+  const int nbytes = n > 0 ? (n - 1) * st2 + 2 * D : 0;
+  const auto krs = make_rsrc(a.k_cache + base, nbytes);
+  const auto vrs = make_rsrc(a.v_cache + base, nbytes);
 
-  for (int step = 0; step < nsteps; ++step) {
-    const int k0 = lo + step * kStepKeys + wave * kWaveKeys;   // first key of this wave
+  // K fragment kb (16 keys) x cc (32 d): lane holds key kb*16 + col, d = 32cc + 8*lgrp
+  int k_off[NCC];
+#pragma unroll
+  for (int cc = 0; cc < NCC; ++cc) k_off[cc] = col * st2 + (32 * cc + 8 * lgrp) * 2;
+  // V DMA: lane fills slot 64*i + lane = (row, physical chunk) of the sub-tile
+  int v_goff[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int s = 64 * i + lane, row = s / DC;
+    v_goff[i] = row * st2 + ((s % DC) ^ dv_swz(row)) * 16;
+  }
+  // V^T transposing reads: row 32j + 16t + 4*lgrp + (col >> 2), d = 16*db + 4*(col & 3)
+  int v_roff[4];
+#pragma unroll
+  for (int dbp = 0; dbp < 4; ++dbp) {
+    const int row = 4 * lgrp + (col >> 2);
+    const int cl = 2 * dbp + ((col & 3) >> 1);
+    v_roff[dbp] = row * D + ((cl ^ dv_swz(row)) * 8) + 4 * (col & 1);
+  }
+  uint16_t* vbuf = smem + wave * 2 * TILE;
 
-    // K fragments (A operand: row = key, k = d) straight from the cache
-    u32x4_t kf[4][D / 32];
+  auto load_k = [&](int st, u32x4_t (&kf)[4][NCC]) {
+    const int off = st * kSub * st2;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = k0 + kb * 16 + col;
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int cc = 0; cc < D / 32; ++cc)
-        kf[kb][cc] = key < hi ? load16(kbase + (int64_t)key * a.kv_st + 32 * cc + 8 * lgrp)
-                              : u32x4_t{0, 0, 0, 0};
-    }
-    // V rows, two consecutive keys x 8 d per item
-    u32x4_t vr[VIT][2];
+      for (int cc = 0; cc < NCC; ++cc) kf[kb][cc] = buffer_load16<kNonTemporal>(krs, k_off[cc] + kb * 16 * st2 + off);
+  };
+  auto dma_v = [&](int st, int buf) {
+    const int off = st * kSub * st2;
 #pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int it = lane + 64 * i;
-      const int key = k0 + 2 * (it / DC);
-      const int ch = it % DC;
-      vr[i][0] = key < hi ? load16(vbase + (int64_t)key * a.kv_st + ch * 8) : u32x4_t{0, 0, 0, 0};
-      vr[i][1] = key + 1 < hi ? load16(vbase + (int64_t)(key + 1) * a.kv_st + ch * 8)
-                              : u32x4_t{0, 0, 0, 0};
-    }
-
-    // S^T = K Q^T
+    for (int i = 0; i < NDMA; ++i) buffer_load16_lds<kNonTemporal>(vrs, vbuf + buf * TILE + i * 512, v_goff[i] + off);
+  };
+  auto compute = [&](int st, int buf, const u32x4_t (&kf)[4][NCC]) {
     f32x4_t s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       s[kb] = f32x4_t{};
 #pragma unroll
-      for (int cc = 0; cc < D / 32; ++cc) s[kb] = mfma_16x16x32(kf[kb][cc], qf[cc], s[kb]);
+      for (int cc = 0; cc < NCC; ++cc) s[kb] = mfma_16x16x32(kf[kb][cc], qf[cc], s[kb]);
     }
-
-    // V -> transposed LDS tile (this wave's region)
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int it = lane + 64 * i;
-      const int key = 2 * (it / DC);
-      const int ch = it % DC;
-      const int pos = vt_pos16(key);
-      const int pch = pos >> 3, within = pos & 7;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = ch * 8 + e;
-        const uint32_t x = vr[i][0][e >> 1], y = vr[i][1][e >> 1];
-        const uint32_t w = (e & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-        *reinterpret_cast<uint32_t*>(vt + d * kWaveKeys + ((pch ^ vt_swizzle(d)) * 8) + within) = w;
-      }
-    }
-
-    // mask keys past the chunk end
-    if (k0 + kWaveKeys > hi) {
+    const int k0 = st * kSub;
+    if (k0 + kSub > n) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (k0 + kb * 16 + 4 * lgrp + i >= hi) s[kb][i] = -INFINITY;
+          if (k0 + kb * 16 + 4 * lgrp + i >= n) s[kb][i] = -INFINITY;
     }
-
-    // online softmax update (log2 domain)
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = pair16_max(mx);
-    mx = pair32_max(mx);
+    float mx = max3f(s[0][0], s[0][1], s[0][2]);
+    mx = max3f(mx, s[0][3], s[1][0]);
+    mx = max3f(mx, s[1][1], s[1][2]);
+    mx = max3f(mx, s[1][3], s[2][0]);
+    mx = max3f(mx, s[2][1], s[2][2]);
+    mx = max3f(mx, s[2][3], s[3][0]);
+    mx = max3f(mx, s[3][1], s[3][2]);
+    mx = fmaxf(mx, s[3][3]);
+    mx = pair32_max(pair16_max(mx));
     const float m_new = fmaxf(m, mx * a.scale_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
+    const float alpha = fast_exp2(m - m_new);
+    m = m_new;
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(s[kb][i] * a.scale_log2 - m_use);
+        const float p = fast_exp2(__builtin_fmaf(s[kb][i], a.scale_log2, -m));
         s[kb][i] = p;
         rs += p;
       }
     l = l * alpha + rs;
-    m = m_new;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
-
-    __syncthreads();   // transposed V visible to the whole wave
-
-    // O^T += V^T P^T, 32 keys per MFMA
+    const uint16_t* vt = vbuf + buf * TILE;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       u32x4_t pf;
@@ -195,18 +185,50 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       pf[3] = pack_bf16x2(s[2 * j + 1][2], s[2 * j + 1][3]);
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        const int d = db * 16 + col;
-        const int ch = (4 * j + lgrp) ^ vt_swizzle(d);
-        acc[db] = mfma_16x16x32(*reinterpret_cast<const u32x4_t*>(vt + d * kWaveKeys + ch * 8),
-                                pf, acc[db]);
+        const uint16_t* vp = vt + v_roff[db & 3] + 32 * j * D + (db >> 2) * 64;
+        const u32x2_t v0 = lds_read_tr16(vp);
+        const u32x2_t v1 = lds_read_tr16(vp + 16 * D);
+        const u32x4_t vf = {v0[0], v0[1], v1[0], v1[1]};
+        acc[db] = mfma_16x16x32(vf, pf, acc[db]);
       }
     }
-    __syncthreads();   // V^T reads done before the next step overwrites it
+  };
+
+  // ---- per-wave pipeline over sub-tiles wave, wave+4, ... --------------------
+  // At the top of each pass this wave's copies for sub-tile st are complete;
+  // the copies for st + 4 are then issued and run during st's math.  Two
+  // passes per loop trip so the K register sets swap roles without copies.
+  u32x4_t ka[4][NCC], kb2[4][NCC];
+  int st = wave;
+  if (st < n_sub) {
+    load_k(st, ka);
+    dma_v(st, 0);
+  }
+  int it = 0;
+  while (st < n_sub) {
+    wait_vmem();
+    if (st + 4 < n_sub) {
+      load_k(st + 4, kb2);
+      dma_v(st + 4, (it + 1) & 1);
+    }
+    compute(st, it & 1, ka);
+    st += 4;
+    ++it;
+    if (st >= n_sub) break;
+    wait_vmem();
+    if (st + 4 < n_sub) {
+      load_k(st + 4, ka);
+      dma_v(st + 4, (it + 1) & 1);
+    }
+    compute(st, it & 1, kb2);
+    st += 4;
+    ++it;
   }
 
   // ---- merge the four waves' states through LDS ------------------------------
   l = pair16_sum(l);
   l = pair32_sum(l);
+  __syncthreads();                    // every wave is done with its V buffers
   float* red = reinterpret_cast<float*>(smem);
   float* red_m = red;                 // [4][16]
   float* red_l = red + 64;            // [4][16]
@@ -223,29 +245,45 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 
   for (int item = tid; item < nh * D; item += kThreads) {
     const int qh = item / D, d = item % D;
-    float M = -INFINITY;
+    float M = -__FLT_MAX__;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * 16 + qh]);
     float wsum = 0.f, o = 0.f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = fast_exp2(red_m[w * 16 + qh] - M);
-        wsum += red_l[w * 16 + qh] * f;
-        o += red_o[(w * D + d) * 16 + qh] * f;
-      }
+    for (int w = 0; w < 4; ++w) {
+      const float f = fast_exp2(red_m[w * 16 + qh] - M);
+      wsum += red_l[w * 16 + qh] * f;
+      o += red_o[(w * D + d) * 16 + qh] * f;
     }
     const int64_t row = ((int64_t)b * a.num_q_heads + h0 + qh) * a.num_splits + c;
     a.part_o[row * D + d] = wsum > 0.f ? o / wsum : 0.f;
     if (d == 0) {
-      a.part_m[row] = M == -INFINITY ? -INFINITY : M * kLn2;
+      a.part_m[row] = wsum > 0.f ? M * kLn2 : -INFINITY;
       a.part_d[row] = wsum;
     }
   }
 }
 
+// Wave-wide reductions (64 lanes) for the merge.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// One wave per (b, h) row.  Every load of the row is issued up front: lane c
+// reads chunk c's (m, d), and each lane reads its d column of the first
+// kMergeRegs chunks' outputs; the weights are then broadcast lane to lane.
+constexpr int kMergeRegs = 16;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  constexpr int DL = D / 64;                 // d values per lane
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
   const int lane = threadIdx.x & 63;
@@ -253,24 +291,53 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const float* pm = a.part_m + (int64_t)row * ns;
   const float* pd = a.part_d + (int64_t)row * ns;
   const float* po = a.part_o + (int64_t)row * ns * D;
-  float M = -INFINITY;
-  for (int c = 0; c < ns; ++c) M = fmaxf(M, pm[c]);
-  float W = 0.f;
-  float acc[D / 64] = {};
-  if (M != -INFINITY) {
-    for (int c = 0; c < ns; ++c) {
-      const float mc = pm[c];
-      const float w = mc == -INFINITY ? 0.f : pd[c] * fast_exp2((mc - M) * kLog2e);
-      W += w;
+
+  float ov[kMergeRegs][DL];
 #pragma unroll
-      for (int j = 0; j < D / 64; ++j) acc[j] += w * po[(int64_t)c * D + lane + 64 * j];
+  for (int c = 0; c < kMergeRegs; ++c)
+#pragma unroll
+    for (int j = 0; j < DL; ++j) ov[c][j] = c < ns ? po[c * D + lane + 64 * j] : 0.f;
+
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < ns; c0 += 64) {
+    const int c = c0 + lane;
+    M = fmaxf(M, wave_max(c < ns ? pm[c] : -INFINITY));
+  }
+  float W = 0.f;
+  float acc[DL] = {};
+  if (M != -INFINITY) {
+    for (int c0 = 0; c0 < ns; c0 += 64) {
+      const int c = c0 + lane;
+      const float mc = c < ns ? pm[c] : -INFINITY;
+      const float w = mc == -INFINITY ? 0.f : pd[c] * fast_exp2((mc - M) * kLog2e);
+      W += wave_sum(w);
+      const int cn = min(64, ns - c0);
+      auto wt = [&](int k) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+      };
+      int k = 0;
+      if (c0 == 0) {
+#pragma unroll
+        for (int r = 0; r < kMergeRegs; ++r)
+          if (r < cn) {
+            const float wk = wt(r);
+#pragma unroll
+            for (int j = 0; j < DL; ++j) acc[j] += wk * ov[r][j];
+          }
+        k = kMergeRegs;
+      }
+      for (; k < cn; ++k) {
+        const float wk = wt(k);
+#pragma unroll
+        for (int j = 0; j < DL; ++j) acc[j] += wk * po[(int64_t)(c0 + k) * D + lane + 64 * j];
+      }
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
   const int b = row / a.num_q_heads, h = row % a.num_q_heads;
   uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j) {
+  for (int j = 0; j < DL; ++j) {
     const __bf16 v = (__bf16)(acc[j] * inv);
     op[lane + 64 * j] = __builtin_bit_cast(uint16_t, v);
   }

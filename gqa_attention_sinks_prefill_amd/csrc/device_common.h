@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sinkattn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -72,6 +74,48 @@ __device__ __forceinline__ float pair16_sum(float x) {
 __device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
+
+// Raw buffer resource over `num_bytes` bytes from `base` (dword 3 = the CDNA
+// default data format).  A load whose offset lies past num_bytes returns zero
+// and does not touch memory, which is how tiles are padded at sequence ends.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes, kBufferWord3);
+}
+// Cache policy of a load: 0 = default, kNonTemporal = streaming data that is
+// read once (the "nt" bit).
+constexpr int kNonTemporal = 2;
+template <int kPolicy = 0>
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, kPolicy);
+}
+
+// Direct global -> LDS copy through a buffer resource: every lane moves 16
+// bytes from byte_offset into LDS at lds_base + 16 * lane (lanes past the
+// resource's end write zeros).  Completion is tracked by vmcnt.
+template <int kPolicy = 0>
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                                  int byte_offset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_base, 16, byte_offset, 0, 0, kPolicy);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including the
+// LDS copies above) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element (i & 3) of the 8-byte pieces addressed by lanes
+// 4k + (i >> 2), k = 0..3, as its elements k = 0..3.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
+  s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+// max of three floats in one instruction (v_max3_f32)
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // XOR swizzle of the 16-byte column chunk of a transposed-V LDS row.  Rows
 // d and d+1..d+7 land on distinct bank groups when read down a column, and

@@ -8,9 +8,11 @@ import torch
 # elements: max-abs and mean-abs error against the fp64 oracle.
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
-# lse is computed from fp32 logits and an fp32 denominator (no bf16 rounding of
-# the weights enters it), so it is held to a much tighter absolute bound.
-LSE_ABS = 2e-3
+# lse = m + ln(d).  The kernels accumulate d from the same bf16-rounded
+# weights that multiply V (relative rounding <= 2^-9 each, so the sum is off by
+# a relative <= 2^-9 too), with fp32 logits and fp32 accumulation: |dlse| <=
+# ln(1 + 2^-8) ~ 3.9e-3.
+LSE_ABS = 4e-3
 
 
 def assert_close(gpu: torch.Tensor | np.ndarray, ref: np.ndarray, *, what: str,
