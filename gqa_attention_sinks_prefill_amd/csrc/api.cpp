@@ -74,7 +74,7 @@ int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head
 
   const int group = num_q_heads / num_kv_heads;
   const int hpw = sinkattn::prefill_heads_per_workgroup(group);
-  const int rows = sinkattn::prefill_rows_per_workgroup(group);
+  const int rows = sinkattn::prefill_rows_per_workgroup(group, head_dim);
   const int64_t n_qtiles = (max_seqlen + rows - 1) / rows;
   const int64_t num_blocks = n_qtiles * num_seqs * (num_q_heads / hpw);
   if (num_blocks > 0x7fffffff) return fail(SINK_ATTN_EUNSUPPORTED, "problem too large for one launch");

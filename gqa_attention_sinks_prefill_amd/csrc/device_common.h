@@ -91,13 +91,15 @@ __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, int b
 }
 
 // Direct global -> LDS copy through a buffer resource: every lane moves 16
-// bytes from byte_offset into LDS at lds_base + 16 * lane (lanes past the
-// resource's end write zeros).  Completion is tracked by vmcnt.
+// bytes from byte_offset + wave_offset into LDS at lds_base + 16 * lane (lanes
+// past the resource's end write zeros).  lds_base and wave_offset must be
+// wave-uniform.  Completion is tracked by vmcnt.
 template <int kPolicy = 0>
 __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base,
-                                                  int byte_offset) {
+                                                  int byte_offset, int wave_offset = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)lds_base, 16, byte_offset, 0, 0, kPolicy);
+      r, (__attribute__((address_space(3))) void*)lds_base, 16, byte_offset, wave_offset, 0,
+      kPolicy);
 }
 
 // Wait until this wave's outstanding vector-memory operations (including the
@@ -115,12 +117,13 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 }
 
 // max of three floats in one instruction (v_max3_f32)
+// acc + the two bf16 halves of `packed` (v_dot2 with a pair of ones).
+__device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
+                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+}
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// XOR swizzle of the 16-byte column chunk of a transposed-V LDS row.  Rows
-// d and d+1..d+7 land on distinct bank groups when read down a column, and
-// the eight rows 8c+e (c = 0..7, fixed e) written by one store instruction do
-// too.
-__device__ __forceinline__ int vt_swizzle(int d) { return (d ^ (d >> 3)) & 7; }
 
 }  // namespace sinkattn

@@ -61,7 +61,7 @@ struct MergeArgs {
 
 // Workgroup shape of the prefill kernel for a given GQA group size.
 int prefill_heads_per_workgroup(int group);
-int prefill_rows_per_workgroup(int group);
+int prefill_rows_per_workgroup(int group, int head_dim);
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int64_t num_blocks,
                           hipStream_t stream);

@@ -107,6 +107,24 @@ def test_prefill_ragged_edges_all_rows(Hq, Hkv, D, causal):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_growing_logits_all_rows(D, causal):
+    """Key j of a sequence scaled by 1 + j/8, so the logits' spread grows along
+    the sequence by far more than the sink: the running maximum (the kernel's
+    stabiliser) has to move on many tiles after O already holds partial sums."""
+    lens = [300, 129, 64]
+    inp = _prefill_case(lens, 8, 2, D, seed=11 + D + causal, sink_range=(-1.0, 1.0))
+    pos = torch.cat([torch.arange(n, dtype=torch.float32) for n in lens])
+    k = (inp["k"].float() * (1.0 + pos / 8.0)[None, :, None]).to(torch.bfloat16)
+    inp = dict(inp, k=k)
+    out, lse = _prefill_gpu(inp, causal=causal)
+    o_ref, lse_ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                       inp["cu_seqlens"], causal=causal, scale=1 / math.sqrt(D))
+    assert_close(out.reshape(-1, D), o_ref, what=f"growing-logit prefill D={D}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="growing-logit prefill lse")
+
+
+@pytest.mark.parametrize("D", [64, 128])
 def test_prefill_nhd_kv_layout(D):
     inp = _prefill_case([150, 77], 8, 2, D, seed=7)
     out, _ = _prefill_gpu(inp, kv_layout="nhd", with_lse=False)
