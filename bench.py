@@ -150,8 +150,9 @@ def copy_calibration(dev, reps: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first; the clocks take some 20 ms of load to settle")
     ap.add_argument("--cpu-seconds", type=float, default=45.0,
                     help="host time budget of the oracle baseline (0 disables it)")
     ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
@@ -252,7 +253,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_p, "kernel": "prefill_kernel<64,4>",
+                     "traffic": traffic_p, "kernel": "prefill_kernel<64,4,2>",
                      "algorithmic_flop_per_launch": flops, "mean_launch_ms": round(pre_ms, 4)},
         "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "metric": "decode KV GB/s",
                    "ms": round(split_ms + merge_ms, 4), "split_ms": round(split_ms, 4),
