@@ -53,13 +53,17 @@ namespace {
 constexpr int kThreads = 256;
 constexpr float kMaxTileSum = 65536.f;   // 2^16: bound on a tile's weight sum per row
 
-// Chunk swizzles of the row-major K and V tiles.  K is read 16 bytes per lane
-// down 32 consecutive rows: XOR with row % 8 spreads any 8 rows over all
-// eight 16-byte bank groups.  V is read 8 bytes per lane by the transposing
-// read, four consecutive rows x two adjacent chunks per 16-lane group: XOR with
-// 2 * (row % 4) gives those eight chunk reads eight distinct bank groups.
-__device__ __forceinline__ int k_swz(int row) { return row & 7; }
-__device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
+// Chunk swizzles of the row-major K and V tiles (DC 16-byte chunks per row).
+// The LDS serves 256 bytes (16 chunk slots) per cycle: 16 lanes of a 16-byte
+// read, 32 lanes of an 8-byte one.  K is read 16 bytes per lane down
+// consecutive rows; a row starts at slot (row * DC) % 16, so XOR with
+// (row / (16 / DC)) % DC gives any 16 consecutive rows 16 different slots.
+// V is read 8 bytes per lane by the transposing read, a 64-byte run of each
+// of four consecutive rows per half wave; XOR with (DC / 4) * (row % 4) puts
+// the four runs in four different 64-byte slots.  (rocprofv3 reports no LDS
+// bank conflicts with these.)
+template <int DC> __device__ __forceinline__ int k_swz(int row) { return (row / (16 / DC)) & (DC - 1); }
+template <int DC> __device__ __forceinline__ int v_swz(int row) { return (DC / 4) * (row & 3); }
 
 // Query blocks (of 32 rows) per wave for a head dimension.
 constexpr int query_blocks(int d) { return d == 64 ? 2 : 1; }
@@ -153,8 +157,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
 #pragma unroll
   for (int i = 0; i < DMA; ++i) {
     const int s = 64 * (4 * i + wave) + lane, key = s / DC;
-    k_goff[i] = key * k_st2 + ((s % DC) ^ k_swz(key)) * 16;
-    v_goff[i] = key * v_st2 + ((s % DC) ^ v_swz(key)) * 16;
+    k_goff[i] = key * k_st2 + ((s % DC) ^ k_swz<DC>(key)) * 16;
+    v_goff[i] = key * v_st2 + ((s % DC) ^ v_swz<DC>(key)) * 16;
   }
   // Buffer numbers are compile-time constants (std::integral_constant).
   auto dma_k = [&](int kt, auto buf) {
@@ -174,17 +178,17 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
   // chunk 2c + lhalf.  V^T (transposing read): lane i of a 16-lane group
   // addresses key row 16u + 8t + 4*lhalf + (i >> 2), d = 32db + 16*((lane>>4)&1)
   // + 4*(i & 3).
-  int k_roff[4];
+  int k_roff[D / 16];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) k_roff[c] = lrow * D + (((2 * c + lhalf) ^ k_swz(lrow)) * 8);
-  int v_roff[2];
+  for (int c = 0; c < D / 16; ++c) k_roff[c] = lrow * D + (((2 * c + lhalf) ^ k_swz<DC>(lrow)) * 8);
+  int v_roff[D / 32];
   {
     const int i = lane & 15, gi = (lane >> 4) & 1;
     const int row = 4 * lhalf + (i >> 2);                 // key row within an 8-row group
 #pragma unroll
-    for (int dbp = 0; dbp < 2; ++dbp) {
-      const int cl = 4 * dbp + 2 * gi + ((i & 3) >> 1);   // logical chunk for db = dbp
-      v_roff[dbp] = row * D + ((cl ^ v_swz(row)) * 8) + 4 * (i & 1);
+    for (int db = 0; db < D / 32; ++db) {
+      const int cl = 4 * db + 2 * gi + ((i & 3) >> 1);    // logical chunk for db
+      v_roff[db] = row * D + ((cl ^ v_swz<DC>(row)) * 8) + 4 * (i & 1);
     }
   }
   // S^T = K Q^T for one tile: each K operand serves all query blocks
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
 #pragma unroll
       for (int c = 0; c < D / 16; ++c) {
         const u32x4_t kop =
-            *reinterpret_cast<const u32x4_t*>(ks + k_roff[c & 3] + kb * 32 * D + (c >> 2) * 64);
+            *reinterpret_cast<const u32x4_t*>(ks + k_roff[c] + kb * 32 * D);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_32x32x16(kop, qf[qb][c], s[qb][kb]);
       }
@@ -310,7 +314,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
     for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* vp = vt + v_roff[db & 1] + 16 * u * D + (db >> 1) * 64;
+        const uint16_t* vp = vt + v_roff[db] + 16 * u * D;
         const u32x2_t lo = lds_read_tr16(vp);
         const u32x2_t hi = lds_read_tr16(vp + 8 * D);
         vf[u][db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
       for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const uint16_t* vp = vt + v_roff[db & 1] + 16 * u * D + (db >> 1) * 64;
+          const uint16_t* vp = vt + v_roff[db] + 16 * u * D;
           const u32x2_t lo = lds_read_tr16(vp);
           const u32x2_t hi = lds_read_tr16(vp + 8 * D);
           const u32x4_t vf = {lo[0], lo[1], hi[0], hi[1]};
