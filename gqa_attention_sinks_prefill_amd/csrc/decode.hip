@@ -37,10 +37,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSub = 64;                      // keys per sub-tile
 
-// Chunk swizzle of the row-major V sub-tile: a transposing read covers four
-// consecutive rows x two adjacent 16-byte chunks per 16-lane group, and XOR
-// with 2 * (row % 4) puts those eight chunk reads in eight bank groups.
-__device__ __forceinline__ int dv_swz(int row) { return 2 * (row & 3); }
+// Chunk swizzle of the row-major V sub-tile (DC 16-byte chunks per row).  The
+// LDS serves 16 chunk slots (256 bytes) per cycle, i.e. 32 lanes of a
+// transposing 8-byte read: a 32-byte run of each of eight consecutive rows.
+// A row starts at slot (row * DC) % 16; XOR with 2 * ((row / (16 / DC)) %
+// (DC / 2)) gives the eight runs eight different 32-byte slots.
+template <int DC> __device__ __forceinline__ int dv_swz(int row) {
+  return 2 * ((row / (16 / DC)) & (DC / 2 - 1));
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
@@ -109,15 +113,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
     const int s = 64 * i + lane, row = s / DC;
-    v_goff[i] = row * st2 + ((s % DC) ^ dv_swz(row)) * 16;
+    v_goff[i] = row * st2 + ((s % DC) ^ dv_swz<DC>(row)) * 16;
   }
   // V^T transposing reads: row 32j + 16t + 4*lgrp + (col >> 2), d = 16*db + 4*(col & 3)
-  int v_roff[4];
+  int v_roff[D / 16];
 #pragma unroll
-  for (int dbp = 0; dbp < 4; ++dbp) {
+  for (int db = 0; db < D / 16; ++db) {
     const int row = 4 * lgrp + (col >> 2);
-    const int cl = 2 * dbp + ((col & 3) >> 1);
-    v_roff[dbp] = row * D + ((cl ^ dv_swz(row)) * 8) + 4 * (col & 1);
+    const int cl = 2 * db + ((col & 3) >> 1);
+    v_roff[db] = row * D + ((cl ^ dv_swz<DC>(row)) * 8) + 4 * (col & 1);
   }
   uint16_t* vbuf = smem + wave * 2 * TILE;
 
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       pf[3] = pack_bf16x2(s[2 * j + 1][2], s[2 * j + 1][3]);
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        const uint16_t* vp = vt + v_roff[db & 3] + 32 * j * D + (db >> 2) * 64;
+        const uint16_t* vp = vt + v_roff[db] + 32 * j * D;
         const u32x2_t v0 = lds_read_tr16(vp);
         const u32x2_t v1 = lds_read_tr16(vp + 16 * D);
         const u32x4_t vf = {v0[0], v0[1], v1[0], v1[1]};
