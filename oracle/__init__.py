@@ -60,6 +60,10 @@ def _load():
                                   _P, _I32, _P, _I32, _I32, _I32, _F64,
                                   _P, _I64, _I32, _P, _P, _P]
     lib.oracle_decode.restype = _I32
+    lib.oracle_decode_multi.argtypes = [_P, _I64, _I64, _I64, _P, _P, _I64, _I64, _I64,
+                                        _P, _I32, _I32, _P, _I32, _I32, _I32, _F64,
+                                        _P, _I64, _I32, _P, _P, _P]
+    lib.oracle_decode_multi.restype = _I32
     lib.oracle_chunk_states.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I64, _I64,
                                         _P, _I32, _P, _I32, _I32, _I32, _F64,
                                         _I32, _I32, _I32, _P, _I64, _I32, _P, _P, _P]
@@ -170,6 +174,40 @@ def decode(q, k_cache, v_cache, seq_lens, sinks, *, scale=None, rows=None, threa
         threads or default_threads(), o.ctypes.data, lse.ctypes.data, share.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
+    return o, lse, share
+
+
+def decode_multi(q, k_cache, v_cache, seq_lens, sinks, *, scale=None, rows=None, threads=None):
+    """Multi-token decode: q_len new tokens per request, at the end of its cache.
+
+    q: [B, q_len, Hq, D] bf16; new token t of request b sees cached tokens
+    0 .. seq_lens[b] - q_len + t.  Caches as in decode().  rows: (b, t, h)
+    triples, default all in (b, t, h) order.  Returns (o [n, D], lse [n],
+    sink_share [n]) float64.
+    """
+    q, k_cache, v_cache = _bf16(q), _bf16(k_cache), _bf16(v_cache)
+    if k_cache.stride() != v_cache.stride():
+        raise ValueError("K and V caches must share strides")
+    B, q_len, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    sinks = sinks.to(torch.float32).contiguous()
+    lens = seq_lens.to(torch.int32).contiguous()
+    if rows is None:
+        rows_arr, n = None, B * q_len * Hq
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+        n = rows_arr.shape[0]
+    o = np.zeros((n, D), np.float64)
+    lse = np.zeros(n, np.float64)
+    share = np.zeros(n, np.float64)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = _load().oracle_decode_multi(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), k_cache.data_ptr(),
+        v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+        lens.data_ptr(), B, q_len, sinks.data_ptr(), Hq, Hkv, D, scale, _ptr(rows_arr), n,
+        threads or default_threads(), o.ctypes.data, lse.ctypes.data, share.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_decode_multi rejected its arguments")
     return o, lse, share
 
 

@@ -27,7 +27,9 @@
  *       lse = M + ln Z,   sink share = exp(s_h - M) / Z
  *   Prefill, causal: J = {j : j <= i} within the row's own sequence.
  *   Prefill, non-causal: J = the whole sequence.  Decode: J = the cached
- *   tokens 0 .. len_b - 1 of the request.
+ *   tokens 0 .. len_b - 1 of the request.  Multi-token decode (q_len new
+ *   tokens at the end of the cache): J = tokens 0 .. len_b - q_len + t for
+ *   new token t.
  *
  *   Same section, on the online form: the running maximum m and the running
  *   scale d start from the head's sink (d = 1 is exactly exp(s_h - m) when
@@ -203,6 +205,74 @@ int oracle_decode(const uint16_t *q, int64_t q_sb, int64_t q_sh,
             attend_row(q + b * q_sb + h * q_sh,
                        k_cache + b * kv_sb + g * kv_sh, kv_st,
                        v_cache + b * kv_sb + g * kv_sh, kv_st, seq_lens[b], D, scale,
+                       (double)sinks[h], 1, x, out_o + i * D,
+                       out_lse ? out_lse + i : NULL, out_share ? out_share + i : NULL);
+        }
+        free(x);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Multi-token decode, as the speculative and MTP decoders of "GPT-OSS on day
+ * 0" (section "Internal inference engine") and "Hosting Qwen on Blackwell"
+ * (section "Decoders") need it: q_len new tokens per request, already
+ * appended to the request's cache, verified in one pass.  The pages give no
+ * formula; the reading used is plain causal attention of each new token over
+ * the cache up to and including its own position:
+ *   query t of request b (0 <= t < q_len) sees cached tokens
+ *   0 .. len_b - q_len + t.
+ * q_len = 1 is oracle_decode(); a row that sees no cached token sees only
+ * the sink.
+ *   q: [B, q_len, Hq, D] with strides (q_sb, q_st, q_sh), d unit-stride.
+ *   caches and seq_lens as in oracle_decode().
+ *   rows: nrows triples (b, t, h); NULL with nrows = B*q_len*Hq means all,
+ *   in (b, t, h) order.
+ */
+int oracle_decode_multi(const uint16_t *q, int64_t q_sb, int64_t q_st, int64_t q_sh,
+                        const uint16_t *k_cache, const uint16_t *v_cache,
+                        int64_t kv_sb, int64_t kv_sh, int64_t kv_st,
+                        const int32_t *seq_lens, int B, int q_len, const float *sinks,
+                        int Hq, int Hkv, int D, double scale,
+                        const int64_t *rows, int64_t nrows, int num_threads,
+                        double *out_o, double *out_lse, double *out_share)
+{
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || B < 0 || q_len <= 0) return -1;
+    const int r = Hq / Hkv;
+    int64_t maxlen = 0;
+    for (int b = 0; b < B; ++b) {
+        if (seq_lens[b] < 0) return -1;
+        if (seq_lens[b] > maxlen) maxlen = seq_lens[b];
+    }
+    int bad = 0;
+#ifdef _OPENMP
+    if (num_threads > 0) omp_set_num_threads(num_threads);
+#endif
+#pragma omp parallel reduction(| : bad)
+    {
+        double *x = (double *)malloc(sizeof(double) * (size_t)(maxlen > 0 ? maxlen : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < nrows; ++i) {
+            int b, t, h;
+            if (rows) {
+                b = (int)rows[3 * i];
+                t = (int)rows[3 * i + 1];
+                h = (int)rows[3 * i + 2];
+            } else {
+                b = (int)(i / ((int64_t)q_len * Hq));
+                t = (int)((i / Hq) % q_len);
+                h = (int)(i % Hq);
+            }
+            if (b < 0 || b >= B || t < 0 || t >= q_len || h < 0 || h >= Hq || !x) {
+                bad = 1;
+                continue;
+            }
+            int64_t n = (int64_t)seq_lens[b] - q_len + t + 1;   /* visible tokens */
+            if (n < 0) n = 0;
+            int g = h / r;
+            attend_row(q + b * q_sb + t * q_st + h * q_sh,
+                       k_cache + b * kv_sb + g * kv_sh, kv_st,
+                       v_cache + b * kv_sb + g * kv_sh, kv_st, n, D, scale,
                        (double)sinks[h], 1, x, out_o + i * D,
                        out_lse ? out_lse + i : NULL, out_share ? out_share + i : NULL);
         }

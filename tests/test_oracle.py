@@ -288,3 +288,98 @@ def test_rejects_bad_rows():
         oracle.prefill(q, k, v, torch.zeros(2), cu, rows=[(4, 0)])
     with pytest.raises(ValueError):
         oracle.prefill(q, k, v, torch.zeros(2), cu, rows=[(0, 2)])
+
+
+# ------------------------------------------------------- multi-token decode --
+def _multi_case(g, lens, q_len, Hq, Hkv, D, max_ctx=None):
+    max_ctx = max_ctx or max(lens)
+    B = len(lens)
+    q = _bf16_randn(g, B, q_len, Hq, D)
+    kc = _bf16_randn(g, B, Hkv, max_ctx, D)
+    vc = _bf16_randn(g, B, Hkv, max_ctx, D)
+    return q, kc, vc, torch.tensor(lens, dtype=torch.int32)
+
+
+@pytest.mark.parametrize("q_len", [2, 3, 4])
+def test_multi_token_decode_matches_sdpa_bottom_right_mask(q_len):
+    """New token t of a request with L cached tokens (the q_len new ones last)
+    equals SDPA over [zero key with the sink as additive mask] + keys
+    0..L-q_len+t, the rest masked out."""
+    g = torch.Generator().manual_seed(40 + q_len)
+    Hq, Hkv, D = 8, 2, 32
+    lens = [q_len, 9, 23]
+    q, kc, vc, sl = _multi_case(g, lens, q_len, Hq, Hkv, D)
+    sinks = torch.empty(Hq).uniform_(-3, 3, generator=g)
+    sinks[5] = 20.0
+    scale = 1.0 / math.sqrt(D)
+    o, _, _ = oracle.decode_multi(q, kc, vc, sl, sinks, scale=scale)
+    o = o.reshape(len(lens), q_len, Hq, D)
+    r = Hq // Hkv
+    for b, L in enumerate(lens):
+        ks = torch.cat([torch.zeros(Hkv, 1, D, dtype=kc.dtype), kc[b, :, :L]], 1).repeat_interleave(r, 0)
+        vs = torch.cat([torch.zeros(Hkv, 1, D, dtype=vc.dtype), vc[b, :, :L]], 1).repeat_interleave(r, 0)
+        mask = torch.zeros(Hq, q_len, L + 1, dtype=torch.float64)
+        mask[:, :, 0] = sinks.double()[:, None]
+        for t in range(q_len):
+            mask[:, t, 1 + (L - q_len + t) + 1:] = float("-inf")
+        ref = _sdpa(q[b].transpose(0, 1), ks, vs, causal=False, scale=scale, mask=mask)
+        np.testing.assert_allclose(o[b], ref.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_multi_token_decode_of_a_whole_sequence_is_causal_prefill():
+    """With every cached token new (q_len = L) the rows are those of causal prefill."""
+    g = torch.Generator().manual_seed(44)
+    Hq, Hkv, D, L = 4, 1, 64, 12
+    q, kc, vc, sl = _multi_case(g, [L], L, Hq, Hkv, D)
+    sinks = torch.tensor([-2.0, 0.5, float("-inf"), 3.0])
+    o_m, lse_m, sh_m = oracle.decode_multi(q, kc, vc, sl, sinks)
+    cu = torch.tensor([0, L], dtype=torch.int32)
+    o_p, lse_p, sh_p = oracle.prefill(q[0], kc[0], vc[0], sinks, cu, causal=True)
+    np.testing.assert_allclose(o_m, o_p, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse_m, lse_p, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(sh_m, sh_p, rtol=0, atol=1e-13)
+
+
+def test_multi_token_decode_single_token_is_decode():
+    g = torch.Generator().manual_seed(45)
+    q, kc, vc, sl = _multi_case(g, [1, 17, 40], 1, 8, 8, 16)
+    sinks = torch.empty(8).uniform_(-2, 2, generator=g)
+    o_m, lse_m, _ = oracle.decode_multi(q, kc, vc, sl, sinks)
+    o_d, lse_d, _ = oracle.decode(q[:, 0], kc, vc, sl, sinks)
+    assert np.array_equal(o_m, o_d) and np.array_equal(lse_m, lse_d)
+
+
+def test_multi_token_decode_ignores_tokens_after_its_position():
+    """Changing cached tokens past a new token's position leaves that token's
+    output unchanged; changing its own position changes it."""
+    g = torch.Generator().manual_seed(46)
+    q_len, L = 3, 20
+    q, kc, vc, sl = _multi_case(g, [L], q_len, 4, 2, 16, max_ctx=L + 5)
+    sinks = torch.zeros(4)
+    o0, _, _ = oracle.decode_multi(q, kc, vc, sl, sinks)
+    o0 = o0.reshape(q_len, 4, 16)
+    for t in range(q_len):
+        last = L - q_len + t
+        k2, v2 = kc.clone(), vc.clone()
+        k2[:, :, last + 1:] = _bf16_randn(g, *k2[:, :, last + 1:].shape)
+        v2[:, :, last + 1:] = _bf16_randn(g, *v2[:, :, last + 1:].shape)
+        o1, _, _ = oracle.decode_multi(q, k2, v2, sl, sinks)
+        assert np.array_equal(o1.reshape(q_len, 4, 16)[t], o0[t])
+        k3 = kc.clone()
+        k3[:, :, last] = _bf16_randn(g, *k3[:, :, last].shape)
+        o3, _, _ = oracle.decode_multi(q, k3, vc, sl, sinks)
+        assert not np.allclose(o3.reshape(q_len, 4, 16)[t], o0[t])
+
+
+def test_multi_token_rows_that_see_no_token_see_only_the_sink():
+    g = torch.Generator().manual_seed(47)
+    q_len = 4
+    q, kc, vc, sl = _multi_case(g, [2], q_len, 2, 1, 8, max_ctx=4)
+    sinks = torch.tensor([1.25, float("-inf")])
+    o, lse, share = oracle.decode_multi(q, kc, vc, sl, sinks)
+    o, lse, share = o.reshape(q_len, 2, 8), lse.reshape(q_len, 2), share.reshape(q_len, 2)
+    # tokens t = 0, 1 see 2 - 4 + t + 1 <= 0 cached tokens
+    assert np.all(o[:2] == 0.0)
+    assert np.all(lse[:2, 0] == 1.25) and np.all(share[:2, 0] == 1.0)
+    assert np.all(lse[:2, 1] == -np.inf) and np.all(share[:2, 1] == 0.0)
+    assert np.all(np.isfinite(o[2:])) and np.all(share[2:, 0] < 1.0)
