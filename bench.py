@@ -134,6 +134,41 @@ def varlen_prefill_measurement(dev, stream, reps: int):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def multi_decode_measurement(dev, stream, reps: int):
+    """KV GB/s of multi-token decode (speculative / MTP verification): 64 requests x
+    8192 cached tokens, the last 4 of them new, split 1024 + merge, event-timed."""
+    cfg = wl.MTP_DECODE
+    inp = wl.decode_inputs(cfg)
+    q, kc, vc = inp["q"].to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    lens, sinks = inp["seq_lens"].to(dev), inp["sinks"].to(dev)
+    B, q_len, Hq, D = q.shape
+    ns = cfg.num_splits
+    po = torch.empty(B, q_len, Hq, ns, D, device=dev)
+    pm = torch.empty(B, q_len, Hq, ns, device=dev)
+    pd = torch.empty(B, q_len, Hq, ns, device=dev)
+    out = torch.empty(B, q_len, Hq, D, dtype=torch.bfloat16, device=dev)
+    run = lambda: sa.sink_attn_decode_multi(q, kc, vc, lens, sinks, cfg.split_size, ns,
+                                            scale=cfg.scale, out=out, partials=(po, pm, pd),
+                                            stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+         for _ in range(reps)]
+    for a, b in e:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
+    kv = wl.decode_kv_bytes(inp["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
+    gbs = kv / (ms * 1e-3) / 1e9
+    return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
+            "metric": "multi-token decode KV GB/s (split + merge)", "mean_ms": round(ms, 4),
+            "algorithmic_bytes_per_step": kv,
+            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def copy_calibration(dev, reps: int):
     """A plain device-to-device copy of 1 GiB: reads and writes exactly 2^30
     bytes each, the reference that scales the HBM byte counters."""
@@ -268,7 +303,8 @@ def main():
                    "gcn_arch": getattr(props, "gcnArchName", "")},
     }
     if run_p and not args.no_extra:
-        res["extra"] = [varlen_prefill_measurement(dev, stream, max(3, args.steps // 2))]
+        res["extra"] = [varlen_prefill_measurement(dev, stream, max(3, args.steps // 2)),
+                        multi_decode_measurement(dev, stream, max(3, args.steps // 2))]
     if args.only != "all":
         res["note"] = f"--only {args.only}: the other part of the step was not launched"
     if args.cpu_seconds > 0 and run_p:

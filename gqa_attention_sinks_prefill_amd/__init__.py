@@ -20,15 +20,15 @@ import os
 
 import torch
 
-__all__ = ["sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge_states",
-           "sink_attn_decode", "SinkAttnError", "library_path", "load_library",
-           "EXPORTED_SYMBOLS"]
+__all__ = ["sink_attn_prefill", "sink_attn_decode_split", "sink_attn_decode_multi_split",
+           "sink_attn_merge_states", "sink_attn_decode", "sink_attn_decode_multi",
+           "SinkAttnError", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsinkattn.so")
 _lib = None
 
-EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_decode_split",
+EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_decode_multi_split",
                     "sink_attn_merge_states", "sink_attn_last_error")
 
 
@@ -61,6 +61,10 @@ def load_library():
     lib.sink_attn_decode_split.argtypes = [P, I64, I64, P, P, I64, I64, I64, P, I32, I32, P,
                                            I32, I32, I32, F32, I32, I32, P, P, P, P]
     lib.sink_attn_decode_split.restype = ctypes.c_int
+    lib.sink_attn_decode_multi_split.argtypes = [P, I64, I64, I64, I32, P, P, I64, I64, I64, P,
+                                                 I32, I32, P, I32, I32, I32, F32, I32, I32,
+                                                 P, P, P, P]
+    lib.sink_attn_decode_multi_split.restype = ctypes.c_int
     lib.sink_attn_merge_states.argtypes = [P, P, P, I32, I32, I32, I32, P, I64, I64, P, P]
     lib.sink_attn_merge_states.restype = ctypes.c_int
     lib.sink_attn_last_error.argtypes = []
@@ -180,6 +184,50 @@ def sink_attn_decode_split(q, k_cache, v_cache, seq_lens, sinks, split_size, num
     return part_o, part_m, part_d
 
 
+def sink_attn_decode_multi_split(q, k_cache, v_cache, seq_lens, sinks, split_size,
+                                 num_splits=None, *, max_ctx=None, scale=None, part_o=None,
+                                 part_m=None, part_d=None, stream=None):
+    """Per-chunk states of multi-token decode: q [B, q_len, Hq, D], the q_len new
+    tokens being the last of each request's cache [B, Hkv, max_ctx, D].
+
+    Returns (part_o [B, q_len, Hq, S, D], part_m [B, q_len, Hq, S],
+    part_d [B, q_len, Hq, S]) fp32.
+    """
+    _dev(q, "q", torch.bfloat16, 4)
+    _dev(k_cache, "k_cache", torch.bfloat16, 4)
+    _dev(v_cache, "v_cache", torch.bfloat16, 4)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    _dev(sinks, "sinks", torch.float32, 1)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if q.stride(3) != 1 or k_cache.stride(3) != 1:
+        raise ValueError("q and the caches need unit stride along head_dim")
+    B, q_len, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    max_ctx = k_cache.shape[2] if max_ctx is None else int(max_ctx)
+    if num_splits is None:
+        num_splits = -(-max_ctx // split_size)
+    shape = (B, q_len, Hq, num_splits)
+    if part_o is None:
+        part_o = torch.empty(*shape, D, dtype=torch.float32, device=q.device)
+        part_m = torch.empty(shape, dtype=torch.float32, device=q.device)
+        part_d = torch.empty(shape, dtype=torch.float32, device=q.device)
+    for t, nm, shp in ((part_o, "part_o", shape + (D,)), (part_m, "part_m", shape),
+                       (part_d, "part_d", shape)):
+        _dev(t, nm, torch.float32)
+        if not t.is_contiguous() or tuple(t.shape) != shp:
+            raise ValueError(f"{nm} must be contiguous with shape {shp}")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().sink_attn_decode_multi_split(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), q_len, k_cache.data_ptr(),
+        v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+        seq_lens.data_ptr(), B, max_ctx, sinks.data_ptr(), Hq, Hkv, D, scale, int(split_size),
+        int(num_splits), part_o.data_ptr(), part_m.data_ptr(), part_d.data_ptr(),
+        _stream(stream))
+    _check("sink_attn_decode_multi_split", rc)
+    return part_o, part_m, part_d
+
+
 def sink_attn_merge_states(part_o, part_m, part_d, *, out=None, lse=None, stream=None):
     """Merge chunk states [B, Hq, S, D] into out [B, Hq, D] bf16 (and lse [B, Hq])."""
     _dev(part_o, "part_o", torch.float32, 4)
@@ -216,3 +264,28 @@ def sink_attn_decode(q, k_cache, v_cache, seq_lens, sinks, split_size, num_split
                                         num_splits, max_ctx=max_ctx, scale=scale, part_o=po,
                                         part_m=pm, part_d=pd, stream=stream)
     return sink_attn_merge_states(po, pm, pd, out=out, lse=lse, stream=stream)
+
+
+def sink_attn_decode_multi(q, k_cache, v_cache, seq_lens, sinks, split_size, num_splits=None, *,
+                           max_ctx=None, scale=None, out=None, lse=None, partials=None,
+                           stream=None):
+    """Multi-token decode (speculative / MTP verification): split then merge.
+
+    q [B, q_len, Hq, D]; returns out [B, q_len, Hq, D] bf16 (lse, if given,
+    [B, q_len, Hq] fp32 contiguous).
+    """
+    B, q_len, Hq, D = q.shape
+    po, pm, pd = partials if partials is not None else (None, None, None)
+    po, pm, pd = sink_attn_decode_multi_split(q, k_cache, v_cache, seq_lens, sinks, split_size,
+                                              num_splits, max_ctx=max_ctx, scale=scale,
+                                              part_o=po, part_m=pm, part_d=pd, stream=stream)
+    S = po.shape[3]
+    if out is None:
+        out = torch.empty(B, q_len, Hq, D, dtype=torch.bfloat16, device=q.device)
+    _dev(out, "out", torch.bfloat16, 4)
+    if out.stride(3) != 1 or out.stride(0) != q_len * out.stride(1):
+        raise ValueError("out needs unit d-stride and (request, token) dims that flatten")
+    rows = out.as_strided((B * q_len, Hq, D), (out.stride(1), out.stride(2), 1))
+    sink_attn_merge_states(po.view(B * q_len, Hq, S, D), pm.view(B * q_len, Hq, S),
+                           pd.view(B * q_len, Hq, S), out=rows, lse=lse, stream=stream)
+    return out

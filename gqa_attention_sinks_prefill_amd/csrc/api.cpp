@@ -106,16 +106,18 @@ int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head
                   "prefill");
 }
 
-int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_head,
-                           const void* k_cache, const void* v_cache, int64_t kv_stride_b,
-                           int64_t kv_stride_head, int64_t kv_stride_tok,
-                           const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
-                           const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
-                           int32_t head_dim, float scale, int32_t split_size,
-                           int32_t num_splits, float* part_o, float* part_m,
-                           float* part_d, void* stream) {
+int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                                 int64_t q_stride_head, int32_t q_len,
+                                 const void* k_cache, const void* v_cache, int64_t kv_stride_b,
+                                 int64_t kv_stride_head, int64_t kv_stride_tok,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                                 const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float scale, int32_t split_size,
+                                 int32_t num_splits, float* part_o, float* part_m,
+                                 float* part_d, void* stream) {
   g_err[0] = '\0';
   if (batch < 0 || max_ctx < 0) return fail(SINK_ATTN_EINVAL, "batch and max_ctx must be >= 0");
+  if (q_len < 1) return fail(SINK_ATTN_EINVAL, "q_len must be >= 1 (got %d)", q_len);
   if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
   if (int rc = check_scale(scale)) return rc;
   if (split_size <= 0 || split_size % 64 != 0)
@@ -132,18 +134,23 @@ int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_h
   if (!aligned(seq_lens, 4) || !aligned(sinks, 4) || !aligned(part_o, 4) || !aligned(part_m, 4) ||
       !aligned(part_d, 4))
     return fail(SINK_ATTN_EINVAL, "seq_lens, sinks and the partial buffers must be 4-byte aligned");
-  if (!stride_ok(q_stride_b) || !stride_ok(q_stride_head) || !stride_ok(kv_stride_b) ||
-      !stride_ok(kv_stride_head) || !stride_ok(kv_stride_tok))
+  if (!stride_ok(q_stride_b) || !stride_ok(q_stride_tok) || !stride_ok(q_stride_head) ||
+      !stride_ok(kv_stride_b) || !stride_ok(kv_stride_head) || !stride_ok(kv_stride_tok))
     return fail(SINK_ATTN_EINVAL, "strides must be non-negative multiples of 8 elements");
 
   const int group = num_q_heads / num_kv_heads;
-  const int head_slices = (group + 15) / 16;
+  const int64_t ncols = static_cast<int64_t>(q_len) * group;
+  if (ncols > 0x7fffffff) return fail(SINK_ATTN_EUNSUPPORTED, "problem too large for one launch");
+  const int cols_per_block = 16 * sinkattn::decode_column_blocks(static_cast<int>(ncols), head_dim);
+  const int64_t head_slices = (ncols + cols_per_block - 1) / cols_per_block;
   const int64_t num_blocks = static_cast<int64_t>(batch) * num_kv_heads * head_slices * num_splits;
-  if (num_blocks > 0x7fffffff) return fail(SINK_ATTN_EUNSUPPORTED, "problem too large for one launch");
+  if (ncols > 0x7fffffff || num_blocks > 0x7fffffff)
+    return fail(SINK_ATTN_EUNSUPPORTED, "problem too large for one launch");
 
   sinkattn::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.q_sb = q_stride_b;
+  a.q_st = q_stride_tok;
   a.q_sh = q_stride_head;
   a.k_cache = static_cast<const uint16_t*>(k_cache);
   a.v_cache = static_cast<const uint16_t*>(v_cache);
@@ -158,12 +165,29 @@ int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_h
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = group;
-  a.head_slices = head_slices;
+  a.q_len = q_len;
+  a.ncols = static_cast<int32_t>(ncols);
+  a.head_slices = static_cast<int32_t>(head_slices);
   a.split_size = split_size;
   a.num_splits = num_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
   return launched(sinkattn::launch_decode_split(a, head_dim, num_blocks, static_cast<hipStream_t>(stream)),
                   "decode_split");
+}
+
+int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_head,
+                           const void* k_cache, const void* v_cache, int64_t kv_stride_b,
+                           int64_t kv_stride_head, int64_t kv_stride_tok,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                           const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, float scale, int32_t split_size,
+                           int32_t num_splits, float* part_o, float* part_m,
+                           float* part_d, void* stream) {
+  // one new token per request: the multi-token form with q_len = 1
+  return sink_attn_decode_multi_split(q, q_stride_b, 0, q_stride_head, 1, k_cache, v_cache,
+                                      kv_stride_b, kv_stride_head, kv_stride_tok, seq_lens, batch,
+                                      max_ctx, sinks, num_q_heads, num_kv_heads, head_dim, scale,
+                                      split_size, num_splits, part_o, part_m, part_d, stream);
 }
 
 int sink_attn_merge_states(const float* part_o, const float* part_m, const float* part_d,

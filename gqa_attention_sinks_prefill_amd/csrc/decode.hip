@@ -9,8 +9,13 @@
 // memory traffic, so the kernel is built to stream the cache once.
 //
 // decode_split_kernel: one workgroup (4 waves) per (request b, KV head g,
-// 16-head slice of g's query heads, chunk c).  The K/V of the chunk are read
-// exactly once and serve every query head of the group.  The chunk is cut
+// slice of 16*CB columns, chunk c).  A column is one (new token t, query head of g)
+// pair: one new token per request for plain decode, q_len of them for the
+// multi-token decode of speculative / MTP verification ("GPT-OSS on day 0",
+// section "Internal inference engine"; "Hosting Qwen on Blackwell", section
+// "Decoders"), where new token t -- already in the cache, whose last q_len
+// tokens are the new ones -- sees the cache up to its own position.  The K/V
+// of the chunk are read exactly once and serve every column.  The chunk is cut
 // into 64-key sub-tiles; wave w takes sub-tiles w, w+4, w+8, ... and runs its
 // own pipeline with no workgroup barrier until the final merge:
 //   * K of the next sub-tile is loaded HBM -> registers and V of the next
@@ -18,9 +23,12 @@
 //     buffer) while the current sub-tile is computed; both streams are read
 //     once, so they are loaded non-temporally;
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 d straight
-//     from the registers, B = Q^T of up to 16 heads (padding columns zero);
-//   * the softmax state is per lane (column = head); row max and sum reduce
-//     over the four 16-lane rows with permlane16/32 swaps;
+//     from the registers, B = Q^T of a block of 16 columns (padding columns
+//     zero); each K and V^T operand feeds all CB column blocks, so a chunk is
+//     read once for up to 16*CB columns;
+//   * the softmax state is per lane (one column); row max and sum reduce
+//     over the four 16-lane rows with permlane16/32 swaps; keys past a
+//     column's position are masked in the last sub-tiles;
 //   * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T
 //     accumulators, V^T from the row-major V tile via the transposing LDS read.
 // At the end the 4 waves' states are merged through LDS and the chunk's
@@ -46,13 +54,21 @@ template <int DC> __device__ __forceinline__ int dv_swz(int row) {
   return 2 * ((row / (16 / DC)) & (DC / 2 - 1));
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+// head_dim 64 with up to 2 column blocks: two workgroups per CU (64 KB of LDS
+// each), so 2 waves / SIMD; wider blocks and head_dim 128 need the registers
+// of 1 wave / SIMD.
+template <int D, int CB>
+__global__ __launch_bounds__(kThreads, (D == 64 && CB <= 2) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int DC = D / 8;                  // 16-byte chunks per row
   constexpr int TILE = kSub * D;             // elements of one V sub-tile
   constexpr int NDMA = kSub * DC / 64;       // DMA instructions per V sub-tile
   constexpr int NCC = D / 32;                // 32-d chunks of a K fragment row
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * 2 * TILE];
+  constexpr int NC = 16 * CB;                // columns of a workgroup
+  // LDS: the waves' V double buffers, later reused for the final merge of
+  // the four waves' states (m, l and o of every column, fp32).
+  constexpr int kMergeFloats = 8 * NC + 4 * D * NC;
+  constexpr int kSmemElems = 4 * 2 * TILE > 2 * kMergeFloats ? 4 * 2 * TILE : 2 * kMergeFloats;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kSmemElems];
 
   int unit = blockIdx.x;
   const int c = unit % a.num_splits;
@@ -65,37 +81,45 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int col = lane & 15;           // query head of the slice this lane serves
+  const int col = lane & 15;           // column of each 16-column block this lane serves
   const int lgrp = lane >> 4;          // 16-lane row group 0..3
-  const int h0 = g * a.group + hs * 16;
-  const int nh = min(16, a.group - hs * 16);
-  const bool hvalid = col < nh;
-  const int h = h0 + (hvalid ? col : 0);
+  const int x0 = hs * NC;              // first column of the workgroup
+  const int nx = min(NC, a.ncols - x0);
 
   const int len = a.seq_lens[b];
   const int lo = c * a.split_size;
   const int n = max(min(a.split_size, len - lo), 0);    // keys of this chunk
   const int n_sub = (n + kSub - 1) / kSub;
+  // keys of this chunk visible to every column
+  const int n_all = min(n, len - (a.q_len - 1) - lo);
 
-  // Q^T fragments: column = head, k = d
-  u32x4_t qf[NCC];
-  {
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh + 8 * lgrp;
+  // Per column block: Q^T fragments (column = (new token, head), k = d), the
+  // keys of this chunk the lane's column sees, and the softmax state.  The
+  // sink seeds wave 0 of chunk 0 only, counted once (row group 0).
+  const bool seeded = (c == 0) && (wave == 0);
+  u32x4_t qf[CB][NCC];
+  int n_lane[CB];
+  float m[CB], l[CB];
+  f32x4_t acc[CB][D / 16];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const bool valid = cb * 16 + col < nx;
+    const int x = x0 + (valid ? cb * 16 + col : 0);
+    const int tq = x / a.group;        // new token of the column
+    const int h = g * a.group + x % a.group;
+    n_lane[cb] = min(n, len - (a.q_len - 1 - tq) - lo);
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)tq * a.q_st + (int64_t)h * a.q_sh + 8 * lgrp;
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
-      u32x4_t t = load16(qp + 32 * cc);
-      qf[cc] = hvalid ? t : u32x4_t{0, 0, 0, 0};
+      const u32x4_t t = load16(qp + 32 * cc);
+      qf[cb][cc] = valid ? t : u32x4_t{0, 0, 0, 0};
     }
-  }
-
-  // state: the sink seeds wave 0 of chunk 0 only, counted once (row group 0)
-  const float sink = hvalid ? a.sinks[h] : -INFINITY;
-  const bool seeded = (c == 0) && (wave == 0);
-  float m = seeded ? fmaxf(sink * kLog2e, -__FLT_MAX__) : -__FLT_MAX__;
-  float l = (seeded && lgrp == 0 && sink != -INFINITY) ? 1.f : 0.f;
-  f32x4_t acc[D / 16];
+    const float sink = valid ? a.sinks[h] : -INFINITY;
+    m[cb] = seeded ? fmaxf(sink * kLog2e, -__FLT_MAX__) : -__FLT_MAX__;
+    l[cb] = (seeded && lgrp == 0 && sink != -INFINITY) ? 1.f : 0.f;
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) acc[db] = f32x4_t{};
+    for (int db = 0; db < D / 16; ++db) acc[cb][db] = f32x4_t{};
+  }
 
   // K / V of this chunk through buffer resources (loads past its end read 0)
   const int st2 = (int)(a.kv_st * 2);
@@ -137,63 +161,77 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) buffer_load16_lds<kNonTemporal>(vrs, vbuf + buf * TILE + i * 512, v_goff[i] + off);
   };
+  // One 64-key sub-tile: every K operand and every V^T operand feeds the CB
+  // column blocks' MFMAs.
   auto compute = [&](int st, int buf, const u32x4_t (&kf)[4][NCC]) {
-    f32x4_t s[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = f32x4_t{};
-#pragma unroll
-      for (int cc = 0; cc < NCC; ++cc) s[kb] = mfma_16x16x32(kf[kb][cc], qf[cc], s[kb]);
-    }
-    const int k0 = st * kSub;
-    if (k0 + kSub > n) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (k0 + kb * 16 + 4 * lgrp + i >= n) s[kb][i] = -INFINITY;
-    }
-    float mx = max3f(s[0][0], s[0][1], s[0][2]);
-    mx = max3f(mx, s[0][3], s[1][0]);
-    mx = max3f(mx, s[1][1], s[1][2]);
-    mx = max3f(mx, s[1][3], s[2][0]);
-    mx = max3f(mx, s[2][1], s[2][2]);
-    mx = max3f(mx, s[2][3], s[3][0]);
-    mx = max3f(mx, s[3][1], s[3][2]);
-    mx = fmaxf(mx, s[3][3]);
-    mx = pair32_max(pair16_max(mx));
-    const float m_new = fmaxf(m, mx * a.scale_log2);
-    const float alpha = fast_exp2(m - m_new);
-    m = m_new;
-    float rs = 0.f;
+    f32x4_t s[CB][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(s[kb][i], a.scale_log2, -m));
-        s[kb][i] = p;
-        rs += p;
+      for (int cb = 0; cb < CB; ++cb) {
+        s[cb][kb] = f32x4_t{};
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) s[cb][kb] = mfma_16x16x32(kf[kb][cc], qf[cb][cc], s[cb][kb]);
       }
-    l = l * alpha + rs;
+    const int k0 = st * kSub;
+    if (k0 + kSub > n_all) {
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + kb * 16 + 4 * lgrp + i >= n_lane[cb]) s[cb][kb][i] = -INFINITY;
+    }
+    u32x4_t pf[CB][2];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      f32x4_t (&sc)[4] = s[cb];
+      float mx = max3f(sc[0][0], sc[0][1], sc[0][2]);
+      mx = max3f(mx, sc[0][3], sc[1][0]);
+      mx = max3f(mx, sc[1][1], sc[1][2]);
+      mx = max3f(mx, sc[1][3], sc[2][0]);
+      mx = max3f(mx, sc[2][1], sc[2][2]);
+      mx = max3f(mx, sc[2][3], sc[3][0]);
+      mx = max3f(mx, sc[3][1], sc[3][2]);
+      mx = fmaxf(mx, sc[3][3]);
+      mx = pair32_max(pair16_max(mx));
+      const float m_new = fmaxf(m[cb], mx * a.scale_log2);
+      const float alpha = fast_exp2(m[cb] - m_new);
+      m[cb] = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(sc[kb][i], a.scale_log2, -m_new));
+          sc[kb][i] = p;
+          rs += p;
+        }
+      l[cb] = l[cb] * alpha + rs;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[cb][db][i] *= alpha;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        pf[cb][j][0] = pack_bf16x2(sc[2 * j][0], sc[2 * j][1]);
+        pf[cb][j][1] = pack_bf16x2(sc[2 * j][2], sc[2 * j][3]);
+        pf[cb][j][2] = pack_bf16x2(sc[2 * j + 1][0], sc[2 * j + 1][1]);
+        pf[cb][j][3] = pack_bf16x2(sc[2 * j + 1][2], sc[2 * j + 1][3]);
+      }
+    }
     const uint16_t* vt = vbuf + buf * TILE;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      u32x4_t pf;
-      pf[0] = pack_bf16x2(s[2 * j][0], s[2 * j][1]);
-      pf[1] = pack_bf16x2(s[2 * j][2], s[2 * j][3]);
-      pf[2] = pack_bf16x2(s[2 * j + 1][0], s[2 * j + 1][1]);
-      pf[3] = pack_bf16x2(s[2 * j + 1][2], s[2 * j + 1][3]);
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
         const uint16_t* vp = vt + v_roff[db] + 32 * j * D;
         const u32x2_t v0 = lds_read_tr16(vp);
         const u32x2_t v1 = lds_read_tr16(vp + 16 * D);
         const u32x4_t vf = {v0[0], v0[1], v1[0], v1[1]};
-        acc[db] = mfma_16x16x32(vf, pf, acc[db]);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) acc[cb][db] = mfma_16x16x32(vf, pf[cb][j], acc[cb][db]);
       }
     }
   };
@@ -230,36 +268,44 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   }
 
   // ---- merge the four waves' states through LDS ------------------------------
-  l = pair16_sum(l);
-  l = pair32_sum(l);
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) l[cb] = pair32_sum(pair16_sum(l[cb]));
   __syncthreads();                    // every wave is done with its V buffers
+  static_assert(2 * kMergeFloats <= kSmemElems, "merge buffers must fit in LDS");
   float* red = reinterpret_cast<float*>(smem);
-  float* red_m = red;                 // [4][16]
-  float* red_l = red + 64;            // [4][16]
-  float* red_o = red + 128;           // [4][D][16]
-  if (lgrp == 0) {
-    red_m[wave * 16 + col] = m;
-    red_l[wave * 16 + col] = l;
+  float* red_m = red;                 // [4][NC]
+  float* red_l = red + 4 * NC;        // [4][NC]
+  float* red_o = red + 8 * NC;        // [4][D][NC]
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int xl = cb * 16 + col;
+    if (lgrp == 0) {
+      red_m[wave * NC + xl] = m[cb];
+      red_l[wave * NC + xl] = l[cb];
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red_o[(wave * D + db * 16 + 4 * lgrp + i) * NC + xl] = acc[cb][db][i];
   }
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red_o[(wave * D + db * 16 + 4 * lgrp + i) * 16 + col] = acc[db][i];
   __syncthreads();
 
-  for (int item = tid; item < nh * D; item += kThreads) {
-    const int qh = item / D, d = item % D;
+  for (int item = tid; item < nx * D; item += kThreads) {
+    const int xl = item / D, d = item % D;
+    const int x = x0 + xl;
     float M = -__FLT_MAX__;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * 16 + qh]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * NC + xl]);
     float wsum = 0.f, o = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float f = fast_exp2(red_m[w * 16 + qh] - M);
-      wsum += red_l[w * 16 + qh] * f;
-      o += red_o[(w * D + d) * 16 + qh] * f;
+      const float f = fast_exp2(red_m[w * NC + xl] - M);
+      wsum += red_l[w * NC + xl] * f;
+      o += red_o[(w * D + d) * NC + xl] * f;
     }
-    const int64_t row = ((int64_t)b * a.num_q_heads + h0 + qh) * a.num_splits + c;
+    const int64_t row =
+        (((int64_t)b * a.q_len + x / a.group) * a.num_q_heads + g * a.group + x % a.group) *
+            a.num_splits + c;
     a.part_o[row * D + d] = wsum > 0.f ? o / wsum : 0.f;
     if (d == 0) {
       a.part_m[row] = wsum > 0.f ? M * kLn2 : -INFINITY;
@@ -350,14 +396,29 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 
 }  // namespace
 
+int decode_column_blocks(int ncols, int head_dim) {
+  const int need = (ncols + 15) / 16;
+  const int most = head_dim == 64 ? 4 : 2;   // registers
+  return need <= 1 ? 1 : (need <= 2 ? 2 : most);
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs& a, int64_t num_blocks, hipStream_t stream) {
+  const dim3 grid((unsigned)num_blocks), block(kThreads);
+  switch (decode_column_blocks(a.ncols, D)) {
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, block, 0, stream, a); break;
+    default:
+      if constexpr (D == 64) hipLaunchKernelGGL((decode_split_kernel<D, 4>), grid, block, 0, stream, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,
                                hipStream_t stream) {
-  const dim3 grid((unsigned)num_blocks), block(kThreads);
-  if (head_dim == 64)
-    hipLaunchKernelGGL(decode_split_kernel<64>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<128>, grid, block, 0, stream, a);
-  return hipGetLastError();
+  return head_dim == 64 ? launch_decode_d<64>(a, num_blocks, stream)
+                        : launch_decode_d<128>(a, num_blocks, stream);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {

@@ -29,7 +29,7 @@ struct PrefillArgs {
 
 struct DecodeArgs {
   const uint16_t* q;
-  int64_t q_sb, q_sh;
+  int64_t q_sb, q_st, q_sh;  // request, new-token and head strides
   const uint16_t* k_cache;
   const uint16_t* v_cache;
   int64_t kv_sb, kv_sh, kv_st;
@@ -41,7 +41,9 @@ struct DecodeArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t group;          // query heads per KV head
-  int32_t head_slices;    // ceil(group / 16): 16 query heads per workgroup
+  int32_t q_len;          // new tokens per request (1 for plain decode)
+  int32_t ncols;          // q_len * group columns: (new token, query head)
+  int32_t head_slices;    // ceil(ncols / (16 * column blocks)): workgroups per (b, g, chunk)
   int32_t split_size;
   int32_t num_splits;
   float scale_log2;
@@ -65,6 +67,8 @@ int prefill_rows_per_workgroup(int group, int head_dim);
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int64_t num_blocks,
                           hipStream_t stream);
+// Blocks of 16 columns one decode workgroup serves (1, 2, or up to 4 for head_dim 64).
+int decode_column_blocks(int ncols, int head_dim);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,
                                hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

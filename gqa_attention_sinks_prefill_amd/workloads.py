@@ -21,6 +21,8 @@ sequences (``cu_seqlens`` marks the boundaries); prefill K/V are HND
 ``[Hkv, T, D]``.  Decode Q is ``[B, Hq, D]`` and the KV cache is HND per
 request, ``[B, Hkv, max_ctx, D]``; cache slots at or beyond a request's
 length are filled with NaN so that any read of them shows up in the output.
+Multi-token decode Q is ``[B, q_len, Hq, D]``: the q_len new tokens are the
+last q_len cached tokens of each request.
 """
 from __future__ import annotations
 
@@ -63,6 +65,7 @@ class DecodeConfig:
     split_size: int
     seed: int
     edge_sinks: dict = field(default_factory=dict)
+    q_len: int = 1                 # new tokens per request (speculative / MTP verification)
 
     @property
     def scale(self) -> float:
@@ -87,6 +90,12 @@ SPLIT_DECODE = DecodeConfig("decode_b64_ctx8192_h64kv8_d64_split1024", 64, 8192,
 VARLEN_PREFILL = PrefillConfig("varlen_prefill_16seq_512to6000_h64kv4_d128", None, 16,
                                (512, 6000), 64, 4, 128, (-4.0, 4.0), seed=4,
                                edge_sinks={5: float("-inf")})
+
+
+# Multi-token decode (speculative / MTP verification): the split-decode shape with 4
+# new tokens per request, the last 4 of its 8192 cached tokens.
+MTP_DECODE = DecodeConfig("mtp_decode_b64_q4_ctx8192_h64kv8_d64_split1024", 64, 8192, None,
+                          8192, 64, 8, 64, (-4.0, 4.0), split_size=1024, seed=5, q_len=4)
 
 
 def ragged_decode(batch: int) -> DecodeConfig:
@@ -132,16 +141,22 @@ def prefill_inputs(cfg: PrefillConfig) -> dict:
                 max_seqlen=int(lens.max()) if cfg.num_seqs else 0, total_tokens=T)
 
 
-def decode_inputs(cfg: DecodeConfig, poison: float = float("nan")) -> dict:
-    """CPU tensors for a decode workload; unused cache slots hold ``poison``."""
+def decode_inputs(cfg: DecodeConfig, poison: float = float("nan"), lens=None) -> dict:
+    """CPU tensors for a decode workload; unused cache slots hold ``poison``.
+    ``lens`` (one length per request) overrides the configured lengths."""
     g = torch.Generator("cpu").manual_seed(cfg.seed)
     B, Hq, Hkv, D = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
-    if cfg.ctx is not None:
+    if lens is not None:
+        lens = torch.tensor(list(lens), dtype=torch.int32)
+        if lens.numel() != B or int(lens.max()) > cfg.max_ctx:
+            raise ValueError("lens must give one length <= max_ctx per request")
+    elif cfg.ctx is not None:
         lens = torch.full((B,), cfg.ctx, dtype=torch.int32)
     else:
         lo, hi = cfg.ctx_range
         lens = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
-    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    qshape = (B, Hq, D) if cfg.q_len == 1 else (B, cfg.q_len, Hq, D)
+    q = torch.randn(*qshape, generator=g).to(torch.bfloat16)
     caches = []
     for _ in range(2):                                   # K first, then V
         c = torch.empty(B, Hkv, cfg.max_ctx, D, dtype=torch.bfloat16)

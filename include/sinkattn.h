@@ -126,6 +126,38 @@ int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_h
                            float* part_d, void* stream);
 
 /*
+ * Multi-token decode, split over the KV length: the speculative and MTP
+ * decoders of "GPT-OSS on day 0" (section "Internal inference engine") and
+ * "Hosting Qwen on Blackwell" (section "Decoders") verify q_len new tokens
+ * per request in one pass.  The new tokens are already the last q_len of
+ * the request's cache; new token t (0 <= t < q_len) of request b attends, as
+ * in sink_attn_decode_split, to cached tokens 0 .. seq_lens[b] - q_len + t
+ * (causal among the new tokens).  A row that sees no token sees only the
+ * sink.  q_len = 1 is exactly sink_attn_decode_split.
+ *   q [B, q_len, Hq, D] bf16: new token t of request b, head h at
+ *     q + b*q_stride_b + t*q_stride_tok + h*q_stride_head (d unit-stride).
+ *   caches, seq_lens, sinks, scale, split_size, num_splits: as in
+ *     sink_attn_decode_split.
+ *   part_o [B, q_len, Hq, num_splits, D], part_m / part_d
+ *     [B, q_len, Hq, num_splits] fp32 contiguous (caller-allocated, outputs),
+ *     the same per-chunk states; merge them with sink_attn_merge_states with
+ *     batch = B * q_len (output row (b, t, h) is row (b*q_len + t, h)).
+ * The kernel is meant for small q_len (one workgroup serves 16 (token, head)
+ * columns of a GQA group); any q_len >= 1 is accepted.
+ * Errors: as sink_attn_decode_split, plus SINK_ATTN_EINVAL for q_len < 1 or a
+ * q_stride_tok that is negative or not a multiple of 8.
+ */
+int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                                 int64_t q_stride_head, int32_t q_len,
+                                 const void* k_cache, const void* v_cache, int64_t kv_stride_b,
+                                 int64_t kv_stride_head, int64_t kv_stride_tok,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                                 const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float scale, int32_t split_size,
+                                 int32_t num_splits, float* part_o, float* part_m,
+                                 float* part_d, void* stream);
+
+/*
  * Second half of split-KV decode: merge each row's chunk states by their
  * log-sum-exp weights (the pages state that chunks are formed and that only
  * the first carries the sink; the merge is the exact recombination this
@@ -133,7 +165,8 @@ int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_h
  *            o = sum_c w_c o_c / sum_c w_c,  lse = M + ln sum_c w_c.
  * Chunks with m_c = -inf get weight 0; a row with no weight gives o = 0 and
  * lse = -inf.
- *   part_o, part_m, part_d: as written by sink_attn_decode_split.
+ *   part_o, part_m, part_d: as written by sink_attn_decode_split (or by
+ *     sink_attn_decode_multi_split, with batch = B * q_len).
  *   o [B, Hq, D] bf16 (output): row (b, h) at o + b*o_stride_b + h*o_stride_head.
  *   lse: NULL, or fp32 [B, Hq] contiguous (output).
  */

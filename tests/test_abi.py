@@ -113,6 +113,41 @@ def test_decode_split_empty_batch_is_a_noop():
     assert _decode(batch=0, q=None)[0] == 0
 
 
+def _decode_multi(**kw):
+    a = dict(q=16, q_sb=4 * 4096, q_st=4096, q_sh=64, q_len=4, k=16, v=16,
+             kv_sb=8 * 1024 * 64, kv_sh=1024 * 64, kv_st=64, lens=4, batch=4, max_ctx=1024,
+             sinks=4, hq=64, hkv=8, d=64, scale=0.125, split=256, nsplit=4, po=4, pm=4, pd=4)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_decode_multi_split(
+        a["q"], a["q_sb"], a["q_st"], a["q_sh"], a["q_len"], a["k"], a["v"], a["kv_sb"],
+        a["kv_sh"], a["kv_st"], a["lens"], a["batch"], a["max_ctx"], a["sinks"], a["hq"],
+        a["hkv"], a["d"], a["scale"], a["split"], a["nsplit"], a["po"], a["pm"], a["pd"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(q_len=0), -1, "q_len"),
+    (dict(q_len=-3), -1, "q_len"),
+    (dict(q_st=100), -1, "multiples of 8"),
+    (dict(q_st=-8), -1, "multiples of 8"),
+    (dict(q=None), -1, "null"),
+    (dict(split=96), -1, "split_size"),
+    (dict(nsplit=2), -1, "cover"),
+    (dict(hq=60), -1, "multiple"),
+    (dict(d=32), -2, "head_dim"),
+    (dict(k=40), -1, "aligned"),
+])
+def test_decode_multi_split_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _decode_multi(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_decode_multi_split_empty_batch_is_a_noop():
+    assert _decode_multi(batch=0, q=None)[0] == 0
+
+
 def _merge(**kw):
     a = dict(po=4, pm=4, pd=4, batch=2, hq=8, ns=4, d=64, o=16, o_sb=512, o_sh=64, lse=None)
     a.update(kw)

@@ -274,3 +274,100 @@ def test_decode_strided_query_and_output():
                                 inp["sinks"])
     assert_close(out.reshape(-1, 64), o_ref, what="strided decode O")
     assert torch.isnan(obig[:, :, :64]).all() and torch.isnan(obig[:, :, 128:]).all()
+
+
+# ------------------------------------------------------- multi-token decode --
+def _decode_multi_gpu(inp, split_size, *, lens=None):
+    q = inp["q"].to(DEV)
+    kc, vc = inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    B, q_len, Hq, D = q.shape
+    ns = -(-kc.shape[2] // split_size)
+    po = torch.full((B, q_len, Hq, ns, D), float("nan"), device=DEV)
+    pm = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    pd = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    out = torch.full((B, q_len, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, q_len, Hq), float("nan"), device=DEV)
+    lens = (inp["seq_lens"] if lens is None else lens).to(DEV)
+    sa.sink_attn_decode_multi(q, kc, vc, lens, inp["sinks"].to(DEV), split_size, ns, out=out,
+                              lse=lse, partials=(po, pm, pd))
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _multi_cfg(lens, q_len, Hq, Hkv, D, seed, split, max_ctx=None, edges=None):
+    cfg = wl.DecodeConfig("multi", len(lens), None, (1, 1), max_ctx or max(lens), Hq, Hkv, D,
+                          (-4.0, 4.0), split_size=split, seed=seed, edge_sinks=edges or {},
+                          q_len=q_len)
+    return wl.decode_inputs(cfg, lens=lens)
+
+
+@pytest.mark.parametrize("q_len", [2, 3, 4])
+@pytest.mark.parametrize("Hq,Hkv,D", [(64, 8, 64), (64, 4, 64), (64, 4, 128), (8, 8, 64)])
+def test_decode_multi_all_rows(q_len, Hq, Hkv, D):
+    """q_len new tokens per request against the oracle on every row: lengths
+    equal to q_len (only new tokens), around 64-key sub-tiles and chunk edges;
+    (token, head) columns per KV head from 2 to 64 (one to four 16-column
+    blocks per workgroup, one or two workgroups per chunk)."""
+    lens = [q_len, 5, 64, 65, 257, 1000]
+    inp = _multi_cfg(lens, q_len, Hq, Hkv, D, seed=60 + q_len + Hq + D, split=256,
+                     edges={0: float("-inf"), Hq - 1: 20.0})
+    out, lse = _decode_multi_gpu(inp, 256)
+    o_ref, lse_ref, _ = oracle.decode_multi(inp["q"], inp["k_cache"], inp["v_cache"],
+                                            inp["seq_lens"], inp["sinks"])
+    assert_close(out.reshape(-1, D), o_ref, what=f"multi decode q_len={q_len} Hq={Hq} D={D}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="multi decode lse")
+
+
+@pytest.mark.parametrize("q_len", [8, 16])
+def test_decode_multi_long_drafts(q_len):
+    """Longer draft runs: 64 and 128 columns per KV head."""
+    lens = [q_len, 130, 700]
+    inp = _multi_cfg(lens, q_len, 64, 8, 64, seed=80 + q_len, split=512)
+    out, lse = _decode_multi_gpu(inp, 512)
+    o_ref, lse_ref, _ = oracle.decode_multi(inp["q"], inp["k_cache"], inp["v_cache"],
+                                            inp["seq_lens"], inp["sinks"])
+    assert_close(out.reshape(-1, 64), o_ref, what=f"multi decode q_len={q_len}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what=f"multi decode q_len={q_len} lse")
+
+
+def test_decode_multi_rows_that_see_no_token():
+    """Requests shorter than q_len: the leading new tokens see only the sink."""
+    lens = [1, 2, 3]
+    inp = _multi_cfg(lens, 4, 8, 2, 64, seed=70, split=64, max_ctx=64,
+                     edges={1: float("-inf")})
+    out, lse = _decode_multi_gpu(inp, 64)
+    o_ref, lse_ref, _ = oracle.decode_multi(inp["q"], inp["k_cache"], inp["v_cache"],
+                                            inp["seq_lens"], inp["sinks"])
+    assert_close(out.reshape(-1, 64), o_ref, what="multi decode, short requests")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="multi decode lse, short requests")
+
+
+def test_decode_multi_single_token_matches_decode_split():
+    """q_len = 1 through the multi-token entry point is bitwise plain decode."""
+    cfg = wl.DecodeConfig("one", 6, None, (1, 3000), 3000, 64, 8, 64, (-4.0, 4.0),
+                          split_size=512, seed=71)
+    inp = wl.decode_inputs(cfg)
+    out_d, lse_d, _ = _decode_gpu(inp, 512)
+    multi = dict(inp, q=inp["q"].unsqueeze(1))
+    out_m, lse_m = _decode_multi_gpu(multi, 512)
+    assert torch.equal(out_m[:, 0].view(torch.int16), out_d.view(torch.int16))
+    assert torch.equal(lse_m[:, 0], lse_d)
+
+
+def test_decode_multi_full_config_sampled_rows():
+    """64 requests x 8192 tokens, 4 new tokens each (the bench's multi-token line)."""
+    cfg = wl.MTP_DECODE
+    inp = wl.decode_inputs(cfg)
+    out, lse = _decode_multi_gpu(inp, cfg.split_size)
+    assert not torch.isnan(out).any().item()
+    g = torch.Generator().manual_seed(5)
+    B, q_len, Hq, D = inp["q"].shape
+    rows = sorted({(int(torch.randint(B, (1,), generator=g)), t, int(torch.randint(Hq, (1,), generator=g)))
+                   for t in range(q_len) for _ in range(40)})
+    o_ref, lse_ref, _ = oracle.decode_multi(inp["q"], inp["k_cache"], inp["v_cache"],
+                                            inp["seq_lens"], inp["sinks"], rows=rows)
+    idx = torch.tensor(rows)
+    assert_close(out.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]], o_ref,
+                 what="multi decode full config (sampled rows)")
+    assert_lse_close(lse.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]], lse_ref,
+                     what="multi decode full config lse")
