@@ -56,6 +56,10 @@ def _load():
                                    _P, _P, _I32, _I32, _I32, _I32, _F64, _I32,
                                    _P, _I64, _I32, _P, _P, _P]
     lib.oracle_prefill.restype = _I32
+    lib.oracle_prefill_chunked.argtypes = [_P, _I64, _I64, _P, _I64, _I64, _P, _I64, _I64,
+                                           _P, _P, _P, _I32, _I32, _I32, _I32, _F64, _I32,
+                                           _P, _I64, _I32, _P, _P, _P]
+    lib.oracle_prefill_chunked.restype = _I32
     lib.oracle_decode.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I64, _I64,
                                   _P, _I32, _P, _I32, _I32, _I32, _F64,
                                   _P, _I64, _I32, _P, _P, _P]
@@ -134,6 +138,35 @@ def prefill(q, k, v, sinks, cu_seqlens, *, causal=True, scale=None, rows=None,
         threads or default_threads(), o.ctypes.data, lse.ctypes.data, share.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_prefill rejected its arguments")
+    return o, lse, share
+
+
+def prefill_chunked(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, *, causal=True, scale=None,
+                    rows=None, kv_layout="hnd", threads=None):
+    """Chunked prefill: per sequence, len_q new queries (packed by cu_seqlens_q)
+    against len_k >= len_q keys (packed by cu_seqlens_k), the queries being the
+    sequence's last len_q tokens.  Layouts and return values as prefill()."""
+    q, k, v = _bf16(q), _bf16(k), _bf16(v)
+    Tq, Hq, D = q.shape
+    k_st, k_sh, Hkv = _kv_strides(k, kv_layout)
+    v_st, v_sh, _ = _kv_strides(v, kv_layout)
+    sinks = sinks.to(torch.float32).contiguous()
+    cq = cu_seqlens_q.to(torch.int32).contiguous()
+    ck = cu_seqlens_k.to(torch.int32).contiguous()
+    if cq.numel() != ck.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    rows_arr, n = _rows(rows, Tq * Hq)
+    o = np.zeros((n, D), np.float64)
+    lse = np.zeros(n, np.float64)
+    share = np.zeros(n, np.float64)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = _load().oracle_prefill_chunked(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k_st, k_sh,
+        v.data_ptr(), v_st, v_sh, sinks.data_ptr(), cq.data_ptr(), ck.data_ptr(),
+        cq.numel() - 1, Hq, Hkv, D, scale, int(bool(causal)), _ptr(rows_arr), n,
+        threads or default_threads(), o.ctypes.data, lse.ctypes.data, share.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_prefill_chunked rejected its arguments")
     return o, lse, share
 
 

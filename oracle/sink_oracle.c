@@ -29,7 +29,9 @@
  *   Prefill, non-causal: J = the whole sequence.  Decode: J = the cached
  *   tokens 0 .. len_b - 1 of the request.  Multi-token decode (q_len new
  *   tokens at the end of the cache): J = tokens 0 .. len_b - q_len + t for
- *   new token t.
+ *   new token t.  Chunked prefill (a chunk of len_q queries at the end of a
+ *   sequence of len_k tokens): J = tokens 0 .. len_k - len_q + i for query i
+ *   of the chunk, causal.
  *
  *   Same section, on the online form: the running maximum m and the running
  *   scale d start from the head's sink (d = 1 is exactly exp(s_h - m) when
@@ -158,6 +160,70 @@ int oracle_prefill(const uint16_t *q, int64_t q_st, int64_t q_sh,
             attend_row(q + t * q_st + h * q_sh,
                        k + start * k_st + g * k_sh, k_st,
                        v + start * v_st + g * v_sh, v_st, n, D, scale,
+                       (double)sinks[h], 1, x, out_o + i * D,
+                       out_lse ? out_lse + i : NULL, out_share ? out_share + i : NULL);
+        }
+        free(x);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Chunked prefill: per sequence a chunk of new query tokens against a key
+ * range that holds the sequence's earlier tokens followed by the chunk's
+ * own.  "Hosting Qwen on Blackwell" (section "Prefillers") processes long
+ * inputs on dedicated prefill nodes; the split of one input into chunks is
+ * the plain reading of extending that prefill to a cached prefix: query
+ * token i of the chunk (0 <= i < len_q) sits at position len_k - len_q + i
+ * of the sequence and, causal, sees keys 0 .. len_k - len_q + i (all len_k
+ * keys when non-causal).  cu_seqlens_q == cu_seqlens_k is oracle_prefill().
+ *   q: [Tq, Hq, D] packed by cu_seqlens_q; k, v packed by cu_seqlens_k with
+ *   the strides of oracle_prefill().  Requires len_k >= len_q for every
+ *   sequence.  rows: nrows pairs (global query token t, head h); NULL with
+ *   nrows = Tq*Hq means all, token-major.
+ */
+int oracle_prefill_chunked(const uint16_t *q, int64_t q_st, int64_t q_sh,
+                           const uint16_t *k, int64_t k_st, int64_t k_sh,
+                           const uint16_t *v, int64_t v_st, int64_t v_sh,
+                           const float *sinks, const int32_t *cu_seqlens_q,
+                           const int32_t *cu_seqlens_k, int num_seqs,
+                           int Hq, int Hkv, int D, double scale, int causal,
+                           const int64_t *rows, int64_t nrows, int num_threads,
+                           double *out_o, double *out_lse, double *out_share)
+{
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || num_seqs < 0) return -1;
+    const int r = Hq / Hkv;
+    const int64_t Tq = cu_seqlens_q[num_seqs];
+    int64_t maxlen = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+        int64_t len_q = (int64_t)cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+        int64_t len_k = (int64_t)cu_seqlens_k[s + 1] - cu_seqlens_k[s];
+        if (len_q < 0 || len_k < len_q) return -1;
+        if (len_k > maxlen) maxlen = len_k;
+    }
+    int bad = 0;
+#ifdef _OPENMP
+    if (num_threads > 0) omp_set_num_threads(num_threads);
+#endif
+#pragma omp parallel reduction(| : bad)
+    {
+        double *x = (double *)malloc(sizeof(double) * (size_t)(maxlen > 0 ? maxlen : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t i = 0; i < nrows; ++i) {
+            int64_t t = rows ? rows[2 * i] : i / Hq;
+            int h = rows ? (int)rows[2 * i + 1] : (int)(i % Hq);
+            if (t < 0 || t >= Tq || h < 0 || h >= Hq || !x) { bad = 1; continue; }
+            int s = 0;
+            while (cu_seqlens_q[s + 1] <= t) ++s;     /* the row's sequence */
+            int64_t len_q = (int64_t)cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+            int64_t start_k = cu_seqlens_k[s];
+            int64_t len_k = (int64_t)cu_seqlens_k[s + 1] - start_k;
+            int64_t pos = (len_k - len_q) + (t - cu_seqlens_q[s]);   /* position in the sequence */
+            int64_t n = causal ? pos + 1 : len_k;      /* visible keys 0..n-1 */
+            int g = h / r;
+            attend_row(q + t * q_st + h * q_sh,
+                       k + start_k * k_st + g * k_sh, k_st,
+                       v + start_k * v_st + g * v_sh, v_st, n, D, scale,
                        (double)sinks[h], 1, x, out_o + i * D,
                        out_lse ? out_lse + i : NULL, out_share ? out_share + i : NULL);
         }

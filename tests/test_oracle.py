@@ -383,3 +383,84 @@ def test_multi_token_rows_that_see_no_token_see_only_the_sink():
     assert np.all(lse[:2, 0] == 1.25) and np.all(share[:2, 0] == 1.0)
     assert np.all(lse[:2, 1] == -np.inf) and np.all(share[:2, 1] == 0.0)
     assert np.all(np.isfinite(o[2:])) and np.all(share[2:, 0] < 1.0)
+
+
+# ------------------------------------------------------------ chunked prefill --
+def _chunked_case(g, lens_q, lens_k, Hq, Hkv, D):
+    cq = torch.zeros(len(lens_q) + 1, dtype=torch.int32)
+    cq[1:] = torch.cumsum(torch.tensor(lens_q), 0)
+    ck = torch.zeros(len(lens_k) + 1, dtype=torch.int32)
+    ck[1:] = torch.cumsum(torch.tensor(lens_k), 0)
+    q = _bf16_randn(g, int(cq[-1]), Hq, D)
+    k = _bf16_randn(g, Hkv, int(ck[-1]), D)
+    v = _bf16_randn(g, Hkv, int(ck[-1]), D)
+    return q, k, v, cq, ck
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunked_prefill_matches_sdpa_bottom_right_mask(causal):
+    """Query i of a len_q chunk at the end of len_k keys equals SDPA over
+    [zero key with the sink as additive mask] + keys 0..len_k-len_q+i."""
+    g = torch.Generator().manual_seed(50 + causal)
+    Hq, Hkv, D = 8, 2, 32
+    lens_q, lens_k = [5, 1, 17], [5, 40, 33]
+    q, k, v, cq, ck = _chunked_case(g, lens_q, lens_k, Hq, Hkv, D)
+    sinks = torch.empty(Hq).uniform_(-3, 3, generator=g)
+    sinks[2] = 20.0
+    scale = 1.0 / math.sqrt(D)
+    o, _, _ = oracle.prefill_chunked(q, k, v, sinks, cq, ck, causal=causal, scale=scale)
+    o = o.reshape(-1, Hq, D)
+    r = Hq // Hkv
+    for s_, (lq, lk) in enumerate(zip(lens_q, lens_k)):
+        qs = q[int(cq[s_]):int(cq[s_ + 1])].transpose(0, 1)
+        kk, vv = k[:, int(ck[s_]):int(ck[s_ + 1])], v[:, int(ck[s_]):int(ck[s_ + 1])]
+        ks = torch.cat([torch.zeros(Hkv, 1, D, dtype=k.dtype), kk], 1).repeat_interleave(r, 0)
+        vs = torch.cat([torch.zeros(Hkv, 1, D, dtype=v.dtype), vv], 1).repeat_interleave(r, 0)
+        mask = torch.zeros(Hq, lq, lk + 1, dtype=torch.float64)
+        mask[:, :, 0] = sinks.double()[:, None]
+        if causal:
+            for i in range(lq):
+                mask[:, i, 1 + (lk - lq + i) + 1:] = float("-inf")
+        ref = _sdpa(qs, ks, vs, causal=False, scale=scale, mask=mask).transpose(0, 1)
+        np.testing.assert_allclose(o[int(cq[s_]):int(cq[s_ + 1])], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_chunked_prefill_of_a_split_sequence_equals_one_prefill():
+    """Prefill of a sequence cut into chunks (each chunk against all keys up to
+    its end) gives exactly the rows of one causal prefill of the whole."""
+    g = torch.Generator().manual_seed(52)
+    Hq, Hkv, D, L = 4, 2, 64, 50
+    q, k, v, cu = _packed_prefill(g, [L], Hq, Hkv, D)
+    sinks = torch.tensor([0.5, -1.0, float("-inf"), 3.0])
+    o_full, lse_full, _ = oracle.prefill(q, k, v, sinks, cu)
+    cuts = [0, 13, 14, 37, L]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        cq = torch.tensor([0, b - a], dtype=torch.int32)
+        ck = torch.tensor([0, b], dtype=torch.int32)
+        o_c, lse_c, _ = oracle.prefill_chunked(q[a:b], k[:, :b], v[:, :b], sinks, cq, ck)
+        assert np.array_equal(o_c, o_full[a * Hq:b * Hq]) and np.array_equal(lse_c, lse_full[a * Hq:b * Hq])
+
+
+def test_chunked_prefill_with_equal_lengths_is_prefill_and_single_query_is_decode():
+    g = torch.Generator().manual_seed(53)
+    Hq, Hkv, D = 8, 8, 16
+    q, k, v, cq, ck = _chunked_case(g, [7, 12], [7, 12], Hq, Hkv, D)
+    sinks = torch.empty(Hq).uniform_(-2, 2, generator=g)
+    for causal in (True, False):
+        o_c, lse_c, _ = oracle.prefill_chunked(q, k, v, sinks, cq, ck, causal=causal)
+        o_p, lse_p, _ = oracle.prefill(q, k, v, sinks, cq, causal=causal)
+        assert np.array_equal(o_c, o_p) and np.array_equal(lse_c, lse_p)
+    # one query at the end of 30 keys: the decode of that query over the 30 keys
+    q1, k1, v1, cq1, ck1 = _chunked_case(g, [1], [30], Hq, Hkv, D)
+    o_c, lse_c, _ = oracle.prefill_chunked(q1, k1, v1, sinks, cq1, ck1)
+    o_d, lse_d, _ = oracle.decode(q1, k1.unsqueeze(0), v1.unsqueeze(0),
+                                  torch.tensor([30], dtype=torch.int32), sinks)
+    np.testing.assert_allclose(o_c, o_d, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse_c, lse_d, rtol=0, atol=1e-14)
+
+
+def test_chunked_prefill_rejects_a_chunk_longer_than_its_keys():
+    g = torch.Generator().manual_seed(54)
+    q, k, v, cq, ck = _chunked_case(g, [6], [5], 2, 1, 8)
+    with pytest.raises(ValueError):
+        oracle.prefill_chunked(q, k, v, torch.zeros(2), cq, ck)
