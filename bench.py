@@ -134,6 +134,38 @@ def varlen_prefill_measurement(dev, stream, reps: int):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def chunked_prefill_measurement(dev, stream, reps: int):
+    """TFLOP/s of chunked prefill: 4 sequences of 8192 tokens, the last 2048 of
+    each new (6144 cached keys before them), 64 q / 8 KV heads, d 64, causal."""
+    cfg = wl.CHUNKED_PREFILL
+    inp = wl.chunked_prefill_inputs(cfg, wl.CHUNK_LEN)
+    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+    sinks = inp["sinks"].to(dev)
+    cq, ck = inp["cu_seqlens_q"].to(dev), inp["cu_seqlens_k"].to(dev)
+    out = torch.empty_like(q)
+    run = lambda: sa.sink_attn_prefill_chunked(q, k, v, sinks, cq, ck, inp["max_seqlen_q"],
+                                               causal=True, scale=cfg.scale, out=out,
+                                               stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+         for _ in range(reps)]
+    for a, b in e:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
+    flops = wl.chunked_prefill_flops(inp["seqlens_q"].tolist(), inp["seqlens_k"].tolist(),
+                                     cfg.num_q_heads, cfg.head_dim)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": cfg.name, "value": round(tf, 2), "unit": "TFLOP/s",
+            "mean_launch_ms": round(ms, 4), "algorithmic_flop_per_launch": flops,
+            "roofline": {"bound": "mfma", "peak": round(PEAK_BF16_TFLOPS, 1),
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def multi_decode_measurement(dev, stream, reps: int):
     """KV GB/s of multi-token decode (speculative / MTP verification): 64 requests x
     8192 cached tokens, the last 4 of them new, split 1024 + merge, event-timed."""
@@ -304,6 +336,7 @@ def main():
     }
     if run_p and not args.no_extra:
         res["extra"] = [varlen_prefill_measurement(dev, stream, max(3, args.steps // 2)),
+                        chunked_prefill_measurement(dev, stream, max(3, args.steps // 2)),
                         multi_decode_measurement(dev, stream, max(3, args.steps // 2))]
     if args.only != "all":
         res["note"] = f"--only {args.only}: the other part of the step was not launched"

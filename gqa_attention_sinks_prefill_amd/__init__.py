@@ -20,7 +20,7 @@ import os
 
 import torch
 
-__all__ = ["sink_attn_prefill", "sink_attn_decode_split", "sink_attn_decode_multi_split",
+__all__ = ["sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_split", "sink_attn_decode_multi_split",
            "sink_attn_merge_states", "sink_attn_decode", "sink_attn_decode_multi",
            "SinkAttnError", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
@@ -28,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libsinkattn.so")
 _lib = None
 
-EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_decode_multi_split",
+EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_split", "sink_attn_decode_multi_split",
                     "sink_attn_merge_states", "sink_attn_last_error")
 
 
@@ -58,6 +58,10 @@ def load_library():
     lib.sink_attn_prefill.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, I32, I32,
                                       I32, I32, I32, F32, I32, P, I64, I64, P, P]
     lib.sink_attn_prefill.restype = ctypes.c_int
+    lib.sink_attn_prefill_chunked.argtypes = [P, I64, I64, P, I64, I64, P, I64, I64, P, P, P,
+                                              I32, I32, I32, I32, I32, F32, I32, P, I64, I64,
+                                              P, P]
+    lib.sink_attn_prefill_chunked.restype = ctypes.c_int
     lib.sink_attn_decode_split.argtypes = [P, I64, I64, P, P, I64, I64, I64, P, I32, I32, P,
                                            I32, I32, I32, F32, I32, I32, P, P, P, P]
     lib.sink_attn_decode_split.restype = ctypes.c_int
@@ -99,21 +103,11 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, dim: int | None = None)
     return t
 
 
-def sink_attn_prefill(q, k, v, sinks, cu_seqlens, max_seqlen, *, causal=True, scale=None,
-                      kv_layout="hnd", out=None, lse=None, stream=None):
-    """Sink-attention prefill over packed sequences.
-
-    q: [T, Hq, D] bf16.  k, v: bf16 [Hkv, T, D] for kv_layout="hnd" (default)
-    or [T, Hkv, D] for "nhd"; any strides with unit stride along D.
-    sinks: [Hq] fp32.  cu_seqlens: [S+1] int32 on the GPU.  max_seqlen: int.
-    Returns out [T, Hq, D] bf16 (allocated if not given); fills lse [T, Hq]
-    fp32 when passed.
-    """
+def _prefill_args(q, k, v, sinks, kv_layout, out, lse):
     _dev(q, "q", torch.bfloat16, 3)
     _dev(k, "k", torch.bfloat16, 3)
     _dev(v, "v", torch.bfloat16, 3)
     _dev(sinks, "sinks", torch.float32, 1)
-    _dev(cu_seqlens, "cu_seqlens", torch.int32, 1)
     T, Hq, D = q.shape
     if kv_layout == "hnd":
         Hkv = k.shape[0]
@@ -132,6 +126,22 @@ def sink_attn_prefill(q, k, v, sinks, cu_seqlens, max_seqlen, *, causal=True, sc
         _dev(lse, "lse", torch.float32, 2)
         if not lse.is_contiguous() or tuple(lse.shape) != (T, Hq):
             raise ValueError("lse must be a contiguous [T, Hq] fp32 tensor")
+    return T, Hq, Hkv, D, (k_st, k_sh), (v_st, v_sh), out
+
+
+def sink_attn_prefill(q, k, v, sinks, cu_seqlens, max_seqlen, *, causal=True, scale=None,
+                      kv_layout="hnd", out=None, lse=None, stream=None):
+    """Sink-attention prefill over packed sequences.
+
+    q: [T, Hq, D] bf16.  k, v: bf16 [Hkv, T, D] for kv_layout="hnd" (default)
+    or [T, Hkv, D] for "nhd"; any strides with unit stride along D.
+    sinks: [Hq] fp32.  cu_seqlens: [S+1] int32 on the GPU.  max_seqlen: int.
+    Returns out [T, Hq, D] bf16 (allocated if not given); fills lse [T, Hq]
+    fp32 when passed.
+    """
+    _dev(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    T, Hq, Hkv, D, (k_st, k_sh), (v_st, v_sh), out = _prefill_args(q, k, v, sinks, kv_layout,
+                                                                    out, lse)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     rc = load_library().sink_attn_prefill(
         q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k_st, k_sh,
@@ -140,6 +150,32 @@ def sink_attn_prefill(q, k, v, sinks, cu_seqlens, max_seqlen, *, causal=True, sc
         out.data_ptr(), out.stride(0), out.stride(1),
         lse.data_ptr() if lse is not None else None, _stream(stream))
     _check("sink_attn_prefill", rc)
+    return out
+
+
+def sink_attn_prefill_chunked(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *,
+                              causal=True, scale=None, kv_layout="hnd", out=None, lse=None,
+                              stream=None):
+    """Chunked prefill: per sequence, the queries packed by cu_seqlens_q are the
+    last tokens of a sequence whose keys are packed by cu_seqlens_k (same
+    count of sequences, every chunk no longer than its keys).  Layouts as
+    sink_attn_prefill, with q / out over the query tokens and k / v over the
+    key tokens.
+    """
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    T, Hq, Hkv, D, (k_st, k_sh), (v_st, v_sh), out = _prefill_args(q, k, v, sinks, kv_layout,
+                                                                    out, lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().sink_attn_prefill_chunked(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), k_st, k_sh,
+        v.data_ptr(), v_st, v_sh, sinks.data_ptr(), cu_seqlens_q.data_ptr(),
+        cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1, int(max_seqlen_q), Hq, Hkv, D, scale,
+        int(bool(causal)), out.data_ptr(), out.stride(0), out.stride(1),
+        lse.data_ptr() if lse is not None else None, _stream(stream))
+    _check("sink_attn_prefill_chunked", rc)
     return out
 
 

@@ -48,24 +48,29 @@ extern "C" {
 
 const char* sink_attn_last_error(void) { return g_err; }
 
-int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
-                      const void* k, int64_t k_stride_tok, int64_t k_stride_head,
-                      const void* v, int64_t v_stride_tok, int64_t v_stride_head,
-                      const float* sinks, const int32_t* cu_seqlens, int32_t num_seqs,
-                      int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_dim, float scale, int32_t causal,
-                      void* o, int64_t o_stride_tok, int64_t o_stride_head,
-                      float* lse, void* stream) {
+int sink_attn_prefill_chunked(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                              const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                              const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                              const float* sinks, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t num_seqs,
+                              int32_t max_seqlen_q, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, float scale, int32_t causal,
+                              void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                              float* lse, void* stream) {
+  const int32_t* cu_seqlens = cu_seqlens_q;
+  const int32_t max_seqlen = max_seqlen_q;
   g_err[0] = '\0';
   if (num_seqs < 0 || max_seqlen < 0) return fail(SINK_ATTN_EINVAL, "num_seqs and max_seqlen must be >= 0");
   if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
   if (int rc = check_scale(scale)) return rc;
   if (causal != 0 && causal != 1) return fail(SINK_ATTN_EINVAL, "causal must be 0 or 1");
   if (num_seqs == 0 || max_seqlen == 0) return SINK_ATTN_OK;
-  if (!q || !k || !v || !sinks || !cu_seqlens || !o) return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  if (!q || !k || !v || !sinks || !cu_seqlens || !cu_seqlens_k || !o)
+    return fail(SINK_ATTN_EINVAL, "a required pointer is null");
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
     return fail(SINK_ATTN_EINVAL, "q, k, v and o must be 16-byte aligned");
-  if (!aligned(sinks, 4) || !aligned(cu_seqlens, 4) || (lse && !aligned(lse, 4)))
+  if (!aligned(sinks, 4) || !aligned(cu_seqlens, 4) || !aligned(cu_seqlens_k, 4) ||
+      (lse && !aligned(lse, 4)))
     return fail(SINK_ATTN_EINVAL, "sinks, cu_seqlens and lse must be 4-byte aligned");
   if (!stride_ok(q_stride_tok) || !stride_ok(q_stride_head) || !stride_ok(k_stride_tok) ||
       !stride_ok(k_stride_head) || !stride_ok(v_stride_tok) || !stride_ok(v_stride_head) ||
@@ -91,6 +96,7 @@ int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head
   a.v_sh = v_stride_head;
   a.sinks = sinks;
   a.cu_seqlens = cu_seqlens;
+  a.cu_seqlens_k = cu_seqlens_k;
   a.o = static_cast<uint16_t*>(o);
   a.o_st = o_stride_tok;
   a.o_sh = o_stride_head;
@@ -104,6 +110,22 @@ int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head
   a.scale_log2 = scale * 1.4426950408889634f;
   return launched(sinkattn::launch_prefill(a, head_dim, num_blocks, static_cast<hipStream_t>(stream)),
                   "prefill");
+}
+
+int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                      const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                      const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                      const float* sinks, const int32_t* cu_seqlens, int32_t num_seqs,
+                      int32_t max_seqlen, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, float scale, int32_t causal,
+                      void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                      float* lse, void* stream) {
+  // every sequence's queries are all of its tokens: the chunked form with
+  // one boundary table for both
+  return sink_attn_prefill_chunked(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head,
+                                   v, v_stride_tok, v_stride_head, sinks, cu_seqlens, cu_seqlens,
+                                   num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim,
+                                   scale, causal, o, o_stride_tok, o_stride_head, lse, stream);
 }
 
 int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,

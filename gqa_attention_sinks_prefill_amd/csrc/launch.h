@@ -14,7 +14,8 @@ struct PrefillArgs {
   const uint16_t* v;
   int64_t v_st, v_sh;
   const float* sinks;
-  const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens;     // query tokens per sequence
+  const int32_t* cu_seqlens_k;   // key tokens per sequence (== cu_seqlens for plain prefill)
   uint16_t* o;
   int64_t o_st, o_sh;
   float* lse;             // [T, Hq] or null

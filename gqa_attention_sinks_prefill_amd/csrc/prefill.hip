@@ -1,4 +1,9 @@
-// Causal / non-causal varlen prefill with a per-head sink logit, gfx950.
+// Causal / non-causal varlen prefill with a per-head sink logit, gfx950, also
+// in chunked form: a chunk of new queries per sequence against keys that hold
+// the sequence's earlier tokens followed by the chunk ("Hosting Qwen on
+// Blackwell", section "Prefillers", processes long inputs on prefill nodes;
+// query i of a chunk of len_q at the end of len_k keys sees keys up to
+// len_k - len_q + i).
 //
 // Method: "GPT-OSS on day 0" (Perplexity blog), section "Kernels for GPT-OSS /
 // Sink-Attention" -- an online softmax whose running maximum starts at the
@@ -103,8 +108,16 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
   }
   const int seq = slot % a.num_seqs;
   const int qtile = a.n_qtiles - 1 - slot / a.num_seqs;
-  const int start = a.cu_seqlens[seq];
-  const int len = a.cu_seqlens[seq + 1] - start;
+  const int start = a.cu_seqlens[seq];                 // first query token
+  const int len = a.cu_seqlens[seq + 1] - start;       // queries of the sequence
+  const int start_k = a.cu_seqlens_k[seq];             // first key token
+  const int len_k = a.cu_seqlens_k[seq + 1] - start_k;
+  // The queries are the last `len` of the sequence's len_k tokens (all of
+  // them for plain prefill): query i sits at position off + i.  A chunk
+  // longer than its keys breaks the interface's precondition; it is skipped
+  // (its outputs are left unwritten) rather than read out of range.
+  const int off = len_k - len;
+  if (off < 0) return;
   const int q0 = qtile * ROWS;
   if (q0 >= len) return;
 
@@ -122,13 +135,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
   for (int qb = 0; qb < QB; ++qb) {
     qrow[qb] = w_row0 + 32 * qb + lrow;
     qvalid[qb] = qrow[qb] < len;
-    lim[qb] = a.causal ? min(qrow[qb], len - 1) : len - 1;
+    lim[qb] = a.causal ? min(off + qrow[qb], len_k - 1) : len_k - 1;
   }
 
-  const int kv_end = a.causal ? min(q0 + ROWS, len) : len;
+  const int kv_end = a.causal ? min(off + q0 + ROWS, len_k) : len_k;
   const int ntiles = (kv_end + BN - 1) / BN;
   // leading tiles that no row of this workgroup needs masked
-  const int nfull = min(a.causal ? (q0 + 1) / BN : ntiles, len / BN);
+  const int nfull = min(a.causal ? (off + q0 + 1) / BN : ntiles, len_k / BN);
 
   // ---- Q^T fragments (B operand: column = query row, k = d) ---------------
   u32x4_t qf[QB][D / 16];
@@ -145,9 +158,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
 
   // ---- K / V buffer resources over the visible keys -------------------------
   const int k_st2 = (int)(a.k_st * 2), v_st2 = (int)(a.v_st * 2);   // bytes per token
-  const auto krs = make_rsrc(a.k + (int64_t)start * a.k_st + (int64_t)g * a.k_sh,
+  const auto krs = make_rsrc(a.k + (int64_t)start_k * a.k_st + (int64_t)g * a.k_sh,
                              (kv_end - 1) * k_st2 + 2 * D);
-  const auto vrs = make_rsrc(a.v + (int64_t)start * a.v_st + (int64_t)g * a.v_sh,
+  const auto vrs = make_rsrc(a.v + (int64_t)start_k * a.v_st + (int64_t)g * a.v_sh,
                              (kv_end - 1) * v_st2 + 2 * D);
 
   // DMA: thread t's i-th copy fills LDS slot (16 bytes) s = 64*(4i + wave) + lane

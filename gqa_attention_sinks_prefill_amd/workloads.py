@@ -92,6 +92,12 @@ VARLEN_PREFILL = PrefillConfig("varlen_prefill_16seq_512to6000_h64kv4_d128", Non
                                edge_sinks={5: float("-inf")})
 
 
+# Chunked prefill: 4 sequences of 8192 tokens whose last 2048 are the new chunk
+# (the earlier 6144 are cached), GPT-OSS heads; use chunked_prefill_inputs(cfg, 2048).
+CHUNKED_PREFILL = PrefillConfig("chunked_prefill_4seq_8192_chunk2048_h64kv8_d64", (8192,) * 4, 4,
+                                None, 64, 8, 64, (-4.0, 4.0), seed=6)
+CHUNK_LEN = 2048
+
 # Multi-token decode (speculative / MTP verification): the split-decode shape with 4
 # new tokens per request, the last 4 of its 8192 cached tokens.
 MTP_DECODE = DecodeConfig("mtp_decode_b64_q4_ctx8192_h64kv8_d64_split1024", 64, 8192, None,
@@ -141,6 +147,34 @@ def prefill_inputs(cfg: PrefillConfig) -> dict:
                 max_seqlen=int(lens.max()) if cfg.num_seqs else 0, total_tokens=T)
 
 
+def chunked_prefill_inputs(cfg: PrefillConfig, chunk: int) -> dict:
+    """CPU tensors for chunked prefill: each sequence of the config (its full
+    length is the key count) gets a query chunk of its last min(chunk, length)
+    tokens.  Q is ``[Tq, Hq, D]`` over the chunks (``cu_seqlens_q``), K/V are
+    HND ``[Hkv, Tk, D]`` over the whole sequences (``cu_seqlens_k``)."""
+    g = torch.Generator("cpu").manual_seed(cfg.seed)
+    if cfg.seqlens is not None:
+        lens_k = torch.tensor(cfg.seqlens, dtype=torch.int32)
+    else:
+        lo, hi = cfg.len_range
+        lens_k = torch.randint(lo, hi + 1, (cfg.num_seqs,), generator=g,
+                               dtype=torch.int64).to(torch.int32)
+    lens_q = torch.clamp(lens_k, max=chunk)
+    cu_q = torch.zeros(cfg.num_seqs + 1, dtype=torch.int32)
+    cu_q[1:] = torch.cumsum(lens_q, 0).to(torch.int32)
+    cu_k = torch.zeros(cfg.num_seqs + 1, dtype=torch.int32)
+    cu_k[1:] = torch.cumsum(lens_k, 0).to(torch.int32)
+    Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
+    Hq, Hkv, D = cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    q = torch.randn(Tq, Hq, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(Hkv, Tk, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(Hkv, Tk, D, generator=g).to(torch.bfloat16)
+    sinks = _sinks(g, Hq, cfg.sink_range, cfg.edge_sinks)
+    return dict(q=q, k=k, v=v, sinks=sinks, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                seqlens_q=lens_q, seqlens_k=lens_k,
+                max_seqlen_q=int(lens_q.max()) if cfg.num_seqs else 0)
+
+
 def decode_inputs(cfg: DecodeConfig, poison: float = float("nan"), lens=None) -> dict:
     """CPU tensors for a decode workload; unused cache slots hold ``poison``.
     ``lens`` (one length per request) overrides the configured lengths."""
@@ -172,6 +206,14 @@ def decode_inputs(cfg: DecodeConfig, poison: float = float("nan"), lens=None) ->
 def prefill_flops(seqlens, num_q_heads: int, head_dim: int, causal: bool = True) -> float:
     """Algorithmic flops: 4*D per visible (query, key) pair (2*D for QK^T, 2*D for PV)."""
     pairs = sum(int(n) * (int(n) + 1) // 2 if causal else int(n) * int(n) for n in seqlens)
+    return 4.0 * head_dim * num_q_heads * pairs
+
+
+def chunked_prefill_flops(seqlens_q, seqlens_k, num_q_heads: int, head_dim: int) -> float:
+    """Algorithmic flops of causal chunked prefill: query i of a chunk of lq at the
+    end of lk keys sees lk - lq + i + 1 keys; 4*D flops per visible pair."""
+    pairs = sum(int(lq) * (int(lk) - int(lq)) + int(lq) * (int(lq) + 1) // 2
+                for lq, lk in zip(seqlens_q, seqlens_k))
     return 4.0 * head_dim * num_q_heads * pairs
 
 

@@ -91,6 +91,34 @@ int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head
                       float* lse, void* stream);
 
 /*
+ * Chunked prefill: per sequence a chunk of len_q new query tokens against
+ * len_k >= len_q keys that hold the sequence's earlier tokens followed by the
+ * chunk's own ("Hosting Qwen on Blackwell", section "Prefillers", prefills
+ * long inputs on dedicated nodes; cutting an input into chunks over a cached
+ * prefix is the plain extension).  Query i of the chunk sits at position
+ * len_k - len_q + i of its sequence; causal = 1 lets it see keys
+ * 0 .. len_k - len_q + i, causal = 0 all len_k keys.  cu_seqlens_q ==
+ * cu_seqlens_k is exactly sink_attn_prefill.
+ *   q, o [Tq, Hq, D] packed by cu_seqlens_q; k, v packed by cu_seqlens_k
+ *       (token t of KV head g at k + t*k_stride_tok + g*k_stride_head).
+ *   cu_seqlens_q, cu_seqlens_k [num_seqs + 1] int32, device.  Precondition:
+ *       both start at 0 and are non-decreasing, every chunk length is at most
+ *       max_seqlen_q and at most its sequence's key count; a sequence that
+ *       breaks the last condition is skipped (its outputs are left unwritten).
+ *   lse: NULL, or fp32 [Tq, Hq] contiguous.
+ *   Other arguments and errors as sink_attn_prefill.
+ */
+int sink_attn_prefill_chunked(const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+                              const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+                              const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+                              const float* sinks, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t num_seqs,
+                              int32_t max_seqlen_q, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, float scale, int32_t causal,
+                              void* o, int64_t o_stride_tok, int64_t o_stride_head,
+                              float* lse, void* stream);
+
+/*
  * First half of split-KV decode: one query token per request against its
  * cached keys, with each request's key range cut into num_splits chunks of
  * split_size tokens ("GPT-OSS on day 0", section "Kernels for GPT-OSS /

@@ -77,6 +77,37 @@ def test_prefill_empty_work_is_a_noop():
     assert _prefill(max_seqlen=0)[0] == 0
 
 
+def _prefill_chunked(**kw):
+    a = dict(q=16, q_st=512, q_sh=64, k=16, k_st=64, k_sh=64 * 256, v=16, v_st=64,
+             v_sh=64 * 256, sinks=4, cuq=4, cuk=4, num_seqs=1, max_seqlen=256, hq=8, hkv=2,
+             d=64, scale=0.125, causal=1, o=16, o_st=512, o_sh=64, lse=None)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_prefill_chunked(a["q"], a["q_st"], a["q_sh"], a["k"], a["k_st"],
+                                       a["k_sh"], a["v"], a["v_st"], a["v_sh"], a["sinks"],
+                                       a["cuq"], a["cuk"], a["num_seqs"], a["max_seqlen"],
+                                       a["hq"], a["hkv"], a["d"], a["scale"], a["causal"],
+                                       a["o"], a["o_st"], a["o_sh"], a["lse"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(cuk=None), -1, "null"),
+    (dict(cuq=None), -1, "null"),
+    (dict(cuk=6), -1, "aligned"),
+    (dict(d=32), -2, "head_dim"),
+    (dict(causal=-1), -1, "causal"),
+])
+def test_prefill_chunked_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _prefill_chunked(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_prefill_chunked_empty_work_is_a_noop():
+    assert _prefill_chunked(num_seqs=0, q=None, cuk=None)[0] == 0
+
+
 def _decode(**kw):
     a = dict(q=16, q_sb=4096, q_sh=64, k=16, v=16, kv_sb=8 * 1024 * 64, kv_sh=1024 * 64,
              kv_st=64, lens=4, batch=4, max_ctx=1024, sinks=4, hq=64, hkv=8, d=64,

@@ -371,3 +371,61 @@ def test_decode_multi_full_config_sampled_rows():
                  what="multi decode full config (sampled rows)")
     assert_lse_close(lse.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]], lse_ref,
                      what="multi decode full config lse")
+
+
+# ------------------------------------------------------------ chunked prefill --
+def _chunked_gpu(inp, *, causal=True):
+    q = inp["q"].to(DEV)
+    k, v = inp["k"].to(DEV), inp["v"].to(DEV)
+    Tq, Hq, D = q.shape
+    out = torch.full((Tq, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((Tq, Hq), float("nan"), dtype=torch.float32, device=DEV)
+    sa.sink_attn_prefill_chunked(q, k, v, inp["sinks"].to(DEV), inp["cu_seqlens_q"].to(DEV),
+                                 inp["cu_seqlens_k"].to(DEV), inp["max_seqlen_q"],
+                                 causal=causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(64, 8), (8, 8), (16, 1)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_chunked_all_rows(Hq, Hkv, D, causal):
+    """Chunks of up to 100 new queries at the end of sequences of 1..700 keys:
+    chunk and prefix lengths around 32/64-key tiles, a chunk that is the whole
+    sequence, one-query chunks."""
+    lens = (1, 33, 64, 100, 131, 700)
+    cfg = wl.PrefillConfig("chunked", lens, len(lens), None, Hq, Hkv, D, (-4.0, 4.0),
+                           seed=90 + Hq + D + causal, edge_sinks={0: float("-inf"), Hq - 1: 20.0})
+    inp = wl.chunked_prefill_inputs(cfg, 100)
+    out, lse = _chunked_gpu(inp, causal=causal)
+    o_ref, lse_ref, _ = oracle.prefill_chunked(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                               inp["cu_seqlens_q"], inp["cu_seqlens_k"],
+                                               causal=causal, scale=1 / math.sqrt(D))
+    assert_close(out.reshape(-1, D), o_ref, what=f"chunked prefill Hq={Hq} Hkv={Hkv} D={D}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="chunked prefill lse")
+
+
+def test_prefill_chunked_full_config_sampled_rows():
+    """4 sequences of 8192 tokens whose last 2048 are the new chunk (the bench line)."""
+    cfg = wl.CHUNKED_PREFILL
+    inp = wl.chunked_prefill_inputs(cfg, wl.CHUNK_LEN)
+    out, lse = _chunked_gpu(inp)
+    assert not torch.isnan(out).any().item()
+    rows = sample_prefill_rows(inp["cu_seqlens_q"], cfg.num_q_heads, n_random=400, seed=6)
+    o_ref, lse_ref, _ = oracle.prefill_chunked(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                               inp["cu_seqlens_q"], inp["cu_seqlens_k"],
+                                               scale=cfg.scale, rows=rows)
+    assert_close(gather_rows(out, rows), o_ref, what="chunked prefill full config (sampled rows)")
+    idx = torch.tensor(rows)
+    assert_lse_close(lse.cpu()[idx[:, 0], idx[:, 1]], lse_ref, what="chunked prefill lse")
+
+
+def test_prefill_chunked_with_equal_boundaries_is_bitwise_prefill():
+    inp = _prefill_case([150, 77, 64], 8, 2, 64, seed=91)
+    out_p, lse_p = _prefill_gpu(inp)
+    chunk = dict(inp, cu_seqlens_q=inp["cu_seqlens"], cu_seqlens_k=inp["cu_seqlens"],
+                 max_seqlen_q=inp["max_seqlen"])
+    out_c, lse_c = _chunked_gpu(chunk)
+    assert torch.equal(out_c.view(torch.int16), out_p.view(torch.int16))
+    assert torch.equal(lse_c, lse_p)
