@@ -289,3 +289,26 @@ def merge_states(o_parts, m_parts, d_parts):
     if rc != 0:
         raise ValueError("oracle_merge_states rejected its arguments")
     return o, lse
+
+
+def kv_append(k_new, v_new, cu_seqlens_new, cache_pos, k_cache, v_cache):
+    """Write new tokens' K/V rows into HND caches, the definition written out.
+
+    "Hosting Qwen on Blackwell", section "Deployment on GB200 NVL72": caches
+    are HND; new rows arrive token-major.  For request b and new token t of
+    its n_b (packed by cu_seqlens_new), slot cache_pos[b] + t of every KV head
+    receives the row; slots outside [0, max_ctx) are not written.
+    k_new, v_new: [T, Hkv, D] bf16 (CPU); caches [B, Hkv, max_ctx, D] bf16.
+    Returns new (k_cache, v_cache) tensors; the inputs are not modified.
+    """
+    kc, vc = k_cache.clone(), v_cache.clone()
+    cu = [int(x) for x in cu_seqlens_new]
+    pos = [int(x) for x in cache_pos]
+    max_ctx = kc.shape[2]
+    for b in range(len(cu) - 1):
+        for t in range(cu[b + 1] - cu[b]):
+            slot = pos[b] + t
+            if 0 <= slot < max_ctx:
+                kc[b, :, slot, :] = k_new[cu[b] + t]
+                vc[b, :, slot, :] = v_new[cu[b] + t]
+    return kc, vc

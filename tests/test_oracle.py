@@ -464,3 +464,58 @@ def test_chunked_prefill_rejects_a_chunk_longer_than_its_keys():
     q, k, v, cq, ck = _chunked_case(g, [6], [5], 2, 1, 8)
     with pytest.raises(ValueError):
         oracle.prefill_chunked(q, k, v, torch.zeros(2), cq, ck)
+
+
+# ------------------------------------------------------------- KV-cache append --
+def _append_case(g, counts, pos, B, Hkv, D, max_ctx):
+    cu = torch.zeros(len(counts) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(counts), 0)
+    T = int(cu[-1])
+    kn, vn = _bf16_randn(g, T, Hkv, D), _bf16_randn(g, T, Hkv, D)
+    kc, vc = _bf16_randn(g, B, Hkv, max_ctx, D), _bf16_randn(g, B, Hkv, max_ctx, D)
+    return kn, vn, cu, torch.tensor(pos, dtype=torch.int32), kc, vc
+
+
+def test_kv_append_element_by_element():
+    """Against a loop over every element, and every unwritten slot unchanged;
+    tokens that would land past the cache end are dropped."""
+    g = torch.Generator().manual_seed(60)
+    B, Hkv, D, max_ctx = 3, 2, 8, 12
+    counts, pos = [3, 0, 5], [0, 4, 9]          # request 2: slots 9..13, the last two dropped
+    kn, vn, cu, cp, kc, vc = _append_case(g, counts, pos, B, Hkv, D, max_ctx)
+    ko, vo = oracle.kv_append(kn, vn, cu, cp, kc, vc)
+    written = set()
+    for b in range(B):
+        for t in range(counts[b]):
+            j = pos[b] + t
+            if j >= max_ctx:
+                continue
+            written.add((b, j))
+            for h in range(Hkv):
+                for d in range(D):
+                    assert ko[b, h, j, d].item() == kn[int(cu[b]) + t, h, d].item()
+                    assert vo[b, h, j, d].item() == vn[int(cu[b]) + t, h, d].item()
+    for b in range(B):
+        for j in range(max_ctx):
+            if (b, j) not in written:
+                assert torch.equal(ko[b, :, j].view(torch.int16), kc[b, :, j].view(torch.int16))
+                assert torch.equal(vo[b, :, j].view(torch.int16), vc[b, :, j].view(torch.int16))
+
+
+def test_kv_append_then_decode_equals_prefill_last_row():
+    """Prefill K/V appended in two pieces into an empty cache: decode over that
+    cache equals the last causal prefill row."""
+    g = torch.Generator().manual_seed(61)
+    Hq, Hkv, D, L = 4, 2, 32, 21
+    q, k, v, cu = _packed_prefill(g, [L], Hq, Hkv, D)
+    sinks = torch.tensor([0.3, -1.0, 2.0, float("-inf")])
+    kc = torch.zeros(1, Hkv, 32, D, dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    kn, vn = k.transpose(0, 1).contiguous(), v.transpose(0, 1).contiguous()   # token-major
+    kc, vc = oracle.kv_append(kn[:13], vn[:13], torch.tensor([0, 13], dtype=torch.int32),
+                              torch.tensor([0], dtype=torch.int32), kc, vc)
+    kc, vc = oracle.kv_append(kn[13:], vn[13:], torch.tensor([0, L - 13], dtype=torch.int32),
+                              torch.tensor([13], dtype=torch.int32), kc, vc)
+    o_d, lse_d, _ = oracle.decode(q[L - 1:L], kc, vc, torch.tensor([L], dtype=torch.int32), sinks)
+    o_p, lse_p, _ = oracle.prefill(q, k, v, sinks, cu, rows=[(L - 1, h) for h in range(Hq)])
+    assert np.array_equal(o_d, o_p) and np.array_equal(lse_d, lse_p)
