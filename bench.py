@@ -166,6 +166,39 @@ def chunked_prefill_measurement(dev, stream, reps: int):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def kv_append_measurement(dev, stream, reps: int):
+    """GB/s (bytes read + written) of appending 1024 new tokens to each of 64
+    requests' HND caches (8 KV heads, d 64, 8192 slots), token-major rows in."""
+    cfg = wl.KV_APPEND
+    counts = [cfg["new"]] * cfg["batch"]
+    inp = wl.kv_append_inputs(counts, cfg["max_ctx"], cfg["num_kv_heads"], cfg["head_dim"],
+                              cfg["seed"])
+    kn, vn = inp["k_new"].to(dev), inp["v_new"].to(dev)
+    cu, pos = inp["cu_seqlens_new"].to(dev), inp["cache_pos"].to(dev)
+    shape = (cfg["batch"], cfg["num_kv_heads"], cfg["max_ctx"], cfg["head_dim"])
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    run = lambda: sa.sink_attn_kv_append(kn, vn, cu, pos, kc, vc, max_new=cfg["new"],
+                                         stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+         for _ in range(reps)]
+    for a, b in e:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
+    moved = 2.0 * 2 * sum(counts) * cfg["num_kv_heads"] * cfg["head_dim"] * 2   # K+V, read + write
+    gbs = moved / (ms * 1e-3) / 1e9
+    return {"workload": cfg["name"], "value": round(gbs, 1), "unit": "GB/s",
+            "metric": "KV-cache append GB/s (bytes read + written)", "mean_ms": round(ms, 4),
+            "algorithmic_bytes": moved,
+            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def multi_decode_measurement(dev, stream, reps: int):
     """KV GB/s of multi-token decode (speculative / MTP verification): 64 requests x
     8192 cached tokens, the last 4 of them new, split 1024 + merge, event-timed."""
@@ -337,7 +370,8 @@ def main():
     if run_p and not args.no_extra:
         res["extra"] = [varlen_prefill_measurement(dev, stream, max(3, args.steps // 2)),
                         chunked_prefill_measurement(dev, stream, max(3, args.steps // 2)),
-                        multi_decode_measurement(dev, stream, max(3, args.steps // 2))]
+                        multi_decode_measurement(dev, stream, max(3, args.steps // 2)),
+                        kv_append_measurement(dev, stream, max(3, args.steps // 2))]
     if args.only != "all":
         res["note"] = f"--only {args.only}: the other part of the step was not launched"
     if args.cpu_seconds > 0 and run_p:

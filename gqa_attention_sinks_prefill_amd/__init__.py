@@ -22,6 +22,7 @@ import torch
 
 __all__ = ["sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_split", "sink_attn_decode_multi_split",
            "sink_attn_merge_states", "sink_attn_decode", "sink_attn_decode_multi",
+           "sink_attn_kv_append",
            "SinkAttnError", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +30,7 @@ _LIB_PATH = os.path.join(_PKG, "libsinkattn.so")
 _lib = None
 
 EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_split", "sink_attn_decode_multi_split",
-                    "sink_attn_merge_states", "sink_attn_last_error")
+                    "sink_attn_merge_states", "sink_attn_kv_append", "sink_attn_last_error")
 
 
 class SinkAttnError(RuntimeError):
@@ -71,6 +72,9 @@ def load_library():
     lib.sink_attn_decode_multi_split.restype = ctypes.c_int
     lib.sink_attn_merge_states.argtypes = [P, P, P, I32, I32, I32, I32, P, I64, I64, P, P]
     lib.sink_attn_merge_states.restype = ctypes.c_int
+    lib.sink_attn_kv_append.argtypes = [P, P, I64, I64, P, P, I32, I32, P, P, I64, I64, I64,
+                                        I32, I32, I32, P]
+    lib.sink_attn_kv_append.restype = ctypes.c_int
     lib.sink_attn_last_error.argtypes = []
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -325,3 +329,37 @@ def sink_attn_decode_multi(q, k_cache, v_cache, seq_lens, sinks, split_size, num
     sink_attn_merge_states(po.view(B * q_len, Hq, S, D), pm.view(B * q_len, Hq, S),
                            pd.view(B * q_len, Hq, S), out=rows, lse=lse, stream=stream)
     return out
+
+
+def sink_attn_kv_append(k_new, v_new, cu_seqlens_new, cache_pos, k_cache, v_cache, *,
+                        max_new=None, stream=None):
+    """Write new tokens' K and V ([T, Hkv, D] token-major, packed by
+    cu_seqlens_new) into the HND caches [B, Hkv, max_ctx, D] at slots
+    cache_pos[b] .. cache_pos[b] + n_b - 1 (in place; returns the caches)."""
+    _dev(k_new, "k_new", torch.bfloat16, 3)
+    _dev(v_new, "v_new", torch.bfloat16, 3)
+    _dev(cu_seqlens_new, "cu_seqlens_new", torch.int32, 1)
+    _dev(cache_pos, "cache_pos", torch.int32, 1)
+    _dev(k_cache, "k_cache", torch.bfloat16, 4)
+    _dev(v_cache, "v_cache", torch.bfloat16, 4)
+    if k_new.stride() != v_new.stride() or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must share shape and strides")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if k_new.stride(2) != 1 or k_cache.stride(3) != 1:
+        raise ValueError("the new rows and the caches need unit stride along head_dim")
+    B, Hkv, max_ctx, D = k_cache.shape
+    S = cu_seqlens_new.numel() - 1
+    if cache_pos.numel() != S or k_new.shape[1] != Hkv or k_new.shape[2] != D:
+        raise ValueError("shapes of the new rows, cu_seqlens_new, cache_pos and caches disagree")
+    if S > B:
+        raise ValueError("more sequences than cache rows")
+    if max_new is None:
+        max_new = k_new.shape[0]
+    rc = load_library().sink_attn_kv_append(
+        k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_new.stride(1),
+        cu_seqlens_new.data_ptr(), cache_pos.data_ptr(), S, int(max_new), k_cache.data_ptr(),
+        v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), max_ctx,
+        Hkv, D, _stream(stream))
+    _check("sink_attn_kv_append", rc)
+    return k_cache, v_cache

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsinkattn.so")
-SOURCES = ["api.cpp", "prefill.hip", "decode.hip"]
+SOURCES = ["api.cpp", "prefill.hip", "decode.hip", "kv_append.hip"]
 ARCH = "gfx950"
 
 

@@ -246,4 +246,53 @@ int sink_attn_merge_states(const float* part_o, const float* part_m, const float
   return launched(sinkattn::launch_merge(a, head_dim, static_cast<hipStream_t>(stream)), "merge_states");
 }
 
+int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride_tok,
+                        int64_t new_stride_head, const int32_t* cu_seqlens_new,
+                        const int32_t* cache_pos, int32_t num_seqs, int32_t max_new,
+                        void* k_cache, void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
+                        int64_t kv_stride_tok, int32_t max_ctx, int32_t num_kv_heads,
+                        int32_t head_dim, void* stream) {
+  g_err[0] = '\0';
+  if (num_seqs < 0 || max_new < 0 || max_ctx < 0)
+    return fail(SINK_ATTN_EINVAL, "num_seqs, max_new and max_ctx must be >= 0");
+  if (num_kv_heads <= 0) return fail(SINK_ATTN_EINVAL, "num_kv_heads must be positive");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SINK_ATTN_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
+  if (num_seqs == 0 || max_new == 0 || max_ctx == 0) return SINK_ATTN_OK;
+  if (!k_new || !v_new || !cu_seqlens_new || !cache_pos || !k_cache || !v_cache)
+    return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(SINK_ATTN_EINVAL, "k_new, v_new and the caches must be 16-byte aligned");
+  if (!aligned(cu_seqlens_new, 4) || !aligned(cache_pos, 4))
+    return fail(SINK_ATTN_EINVAL, "cu_seqlens_new and cache_pos must be 4-byte aligned");
+  if (!stride_ok(new_stride_tok) || !stride_ok(new_stride_head) || !stride_ok(kv_stride_b) ||
+      !stride_ok(kv_stride_head) || !stride_ok(kv_stride_tok))
+    return fail(SINK_ATTN_EINVAL, "strides must be non-negative multiples of 8 elements");
+  if (k_new == k_cache || v_new == v_cache || k_cache == v_cache)
+    return fail(SINK_ATTN_EINVAL, "the caches must not alias each other or the new rows");
+
+  const int tpb = sinkattn::kv_append_tokens_per_block(head_dim);
+  const int64_t token_blocks = (static_cast<int64_t>(max_new) + tpb - 1) / tpb;
+  const int64_t num_blocks = static_cast<int64_t>(num_seqs) * num_kv_heads * token_blocks;
+  if (num_blocks > 0x7fffffff) return fail(SINK_ATTN_EUNSUPPORTED, "problem too large for one launch");
+
+  sinkattn::KvAppendArgs a{};
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.new_st = new_stride_tok;
+  a.new_sh = new_stride_head;
+  a.cu_seqlens_new = cu_seqlens_new;
+  a.cache_pos = cache_pos;
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.kv_sb = kv_stride_b;
+  a.kv_sh = kv_stride_head;
+  a.kv_st = kv_stride_tok;
+  a.max_ctx = max_ctx;
+  a.num_kv_heads = num_kv_heads;
+  a.token_blocks = static_cast<int32_t>(token_blocks);
+  return launched(sinkattn::launch_kv_append(a, head_dim, num_blocks, static_cast<hipStream_t>(stream)),
+                  "kv_append");
+}
+
 }  // extern "C"

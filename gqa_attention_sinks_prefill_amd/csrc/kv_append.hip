@@ -1,0 +1,82 @@
+// Append new tokens' K and V to per-request HND caches, gfx950.
+//
+// "Hosting Qwen on Blackwell" (Perplexity blog), section "Deployment on GB200
+// NVL72": KV caches are kept in HND order -- heads leading, the tokens of one
+// head contiguous -- while the tokens that a prefill or decode step produces
+// arrive token-major (one row of all KV heads per token, as the QKV
+// projection writes them).  Sections "Prefillers" / "Decoders": prefill fills
+// the caches that the decoders then stream.  This kernel moves a batch of new
+// tokens into their requests' caches: new token t of request b, KV head g,
+// goes to cache slot (b, g, cache_pos[b] + t).
+//
+// It is a pure copy (bytes in = bytes out, bit-exact), bound by HBM: one
+// workgroup per (request, KV head, block of new tokens); each thread moves one
+// 16-byte chunk of K and of V per pass, the chunk index fastest so that the
+// stores of consecutive tokens of one head form one contiguous run.  Tokens
+// past the request's count or past the cache end are skipped (device-side
+// lengths cannot be checked on the host).
+#include "device_common.h"
+#include "launch.h"
+
+namespace sinkattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPasses = 4;                    // token rows per thread
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
+  constexpr int DC = D / 8;                   // 16-byte chunks per token row
+  constexpr int TPP = kThreads / DC;          // tokens per pass
+  constexpr int TB = TPP * kPasses;           // tokens per workgroup
+  int unit = blockIdx.x;
+  const int tb = unit % a.token_blocks;
+  unit /= a.token_blocks;
+  const int g = unit % a.num_kv_heads;
+  const int b = unit / a.num_kv_heads;
+
+  const int start = a.cu_seqlens_new[b];
+  const int n = a.cu_seqlens_new[b + 1] - start;
+  const int64_t pos = a.cache_pos[b];
+  const int c = threadIdx.x % DC;
+  const int t0 = tb * TB + threadIdx.x / DC;
+  const int64_t cache_row = (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
+
+  u32x4_t kr[kPasses], vr[kPasses];
+  bool ok[kPasses];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int t = t0 + p * TPP;
+    ok[p] = t < n && pos >= 0 && pos + t < a.max_ctx;
+    if (ok[p]) {
+      const int64_t src = (int64_t)(start + t) * a.new_st + (int64_t)g * a.new_sh + 8 * c;
+      kr[p] = load16(a.k_new + src);
+      vr[p] = load16(a.v_new + src);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    if (ok[p]) {
+      const int64_t dst = cache_row + (pos + t0 + p * TPP) * a.kv_st + 8 * c;
+      *reinterpret_cast<u32x4_t*>(a.k_cache + dst) = kr[p];
+      *reinterpret_cast<u32x4_t*>(a.v_cache + dst) = vr[p];
+    }
+  }
+}
+
+}  // namespace
+
+int kv_append_tokens_per_block(int head_dim) { return kThreads / (head_dim / 8) * kPasses; }
+
+hipError_t launch_kv_append(const KvAppendArgs& a, int head_dim, int64_t num_blocks,
+                            hipStream_t stream) {
+  const dim3 grid((unsigned)num_blocks), block(kThreads);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(kv_append_kernel<64>, grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<128>, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace sinkattn

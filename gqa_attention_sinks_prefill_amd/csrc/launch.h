@@ -62,6 +62,20 @@ struct MergeArgs {
   int32_t num_splits;
 };
 
+struct KvAppendArgs {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t new_st, new_sh;  // token and head strides of the new rows
+  const int32_t* cu_seqlens_new;
+  const int32_t* cache_pos;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int64_t kv_sb, kv_sh, kv_st;
+  int32_t max_ctx;
+  int32_t num_kv_heads;
+  int32_t token_blocks;    // ceil(max_new / tokens per workgroup)
+};
+
 // Workgroup shape of the prefill kernel for a given GQA group size.
 int prefill_heads_per_workgroup(int group);
 int prefill_rows_per_workgroup(int group, int head_dim);
@@ -73,5 +87,8 @@ int decode_column_blocks(int ncols, int head_dim);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,
                                hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+int kv_append_tokens_per_block(int head_dim);
+hipError_t launch_kv_append(const KvAppendArgs& a, int head_dim, int64_t num_blocks,
+                            hipStream_t stream);
 
 }  // namespace sinkattn

@@ -203,6 +203,32 @@ def decode_inputs(cfg: DecodeConfig, poison: float = float("nan"), lens=None) ->
     return dict(q=q, k_cache=caches[0], v_cache=caches[1], seq_lens=lens, sinks=sinks)
 
 
+# KV-cache append: 64 requests each append 1024 new tokens (8 KV heads, d 64,
+# token-major rows as a QKV projection writes them) to HND caches of 8192 slots.
+KV_APPEND = dict(name="kv_append_b64_new1024_kv8_d64_ctx8192", batch=64, new=1024,
+                 num_kv_heads=8, head_dim=64, max_ctx=8192, seed=7)
+
+
+def kv_append_inputs(counts, max_ctx: int, num_kv_heads: int, head_dim: int, seed: int,
+                     pos=None) -> dict:
+    """New K/V rows ``[T, Hkv, D]`` (token-major, packed by ``cu_seqlens_new``)
+    and a first cache slot per request (drawn so the rows fit when ``pos`` is
+    None).  Draw order: positions, K rows, V rows."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    counts = torch.tensor(list(counts), dtype=torch.int32)
+    cu = torch.zeros(counts.numel() + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(counts, 0).to(torch.int32)
+    if pos is None:
+        room = torch.clamp(max_ctx - counts, min=0).to(torch.int64)
+        pos = (torch.rand(counts.numel(), generator=g) * (room + 1).double()).floor().to(torch.int32)
+    else:
+        pos = torch.tensor(list(pos), dtype=torch.int32)
+    T = int(cu[-1])
+    k = torch.randn(T, num_kv_heads, head_dim, generator=g).to(torch.bfloat16)
+    v = torch.randn(T, num_kv_heads, head_dim, generator=g).to(torch.bfloat16)
+    return dict(k_new=k, v_new=v, cu_seqlens_new=cu, cache_pos=pos, counts=counts)
+
+
 def prefill_flops(seqlens, num_q_heads: int, head_dim: int, causal: bool = True) -> float:
     """Algorithmic flops: 4*D per visible (query, key) pair (2*D for QK^T, 2*D for PV)."""
     pairs = sum(int(n) * (int(n) + 1) // 2 if causal else int(n) * int(n) for n in seqlens)

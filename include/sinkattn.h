@@ -203,6 +203,35 @@ int sink_attn_merge_states(const float* part_o, const float* part_m, const float
                            int32_t head_dim, void* o, int64_t o_stride_b,
                            int64_t o_stride_head, float* lse, void* stream);
 
+/*
+ * Append new tokens' K and V to per-request HND caches, the step between
+ * prefill (or a decode step) and the decode that streams the caches
+ * ("Hosting Qwen on Blackwell": section "Deployment on GB200 NVL72" keeps
+ * caches in HND order; sections "Prefillers" / "Decoders": prefill fills the
+ * caches the decoders read).  A pure copy, bit-exact:
+ *   for request b, new token t < cu_seqlens_new[b+1] - cu_seqlens_new[b],
+ *   KV head g:  cache[b, g, cache_pos[b] + t, :] = new[cu_seqlens_new[b] + t, g, :]
+ *   k_new, v_new bf16: token t of KV head g at k_new + t*new_stride_tok +
+ *       g*new_stride_head (token-major [T, Hkv, D]: stride_tok = Hkv*D,
+ *       stride_head = D); d unit-stride.
+ *   cu_seqlens_new [num_seqs + 1] int32, device; cache_pos [num_seqs] int32,
+ *       device (first slot written for each request).
+ *   k_cache, v_cache bf16 (in/out): element (b, g, slot j, d) at
+ *       b*kv_stride_b + g*kv_stride_head + j*kv_stride_tok + d.
+ *   max_new: host-side bound of the new-token counts (sizes the grid).
+ * Slots outside [0, max_ctx) are not written (the tokens that would land there
+ * are dropped); every other cache slot is left unchanged.  The new rows must
+ * not overlap the caches.  num_seqs, max_new or max_ctx = 0 is a no-op.
+ * Errors: as the other calls (null pointers, 16-byte alignment, strides,
+ * head_dim 64 / 128).
+ */
+int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride_tok,
+                        int64_t new_stride_head, const int32_t* cu_seqlens_new,
+                        const int32_t* cache_pos, int32_t num_seqs, int32_t max_new,
+                        void* k_cache, void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
+                        int64_t kv_stride_tok, int32_t max_ctx, int32_t num_kv_heads,
+                        int32_t head_dim, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */
 const char* sink_attn_last_error(void);

@@ -179,6 +179,39 @@ def test_decode_multi_split_empty_batch_is_a_noop():
     assert _decode_multi(batch=0, q=None)[0] == 0
 
 
+def _kv_append(**kw):
+    a = dict(kn=16, vn=32, n_st=512, n_sh=64, cu=4, pos=8, num_seqs=2, max_new=100, kc=48,
+             vc=64, kv_sb=8 * 1024 * 64, kv_sh=1024 * 64, kv_st=64, max_ctx=1024, hkv=8, d=64)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_kv_append(a["kn"], a["vn"], a["n_st"], a["n_sh"], a["cu"], a["pos"],
+                                 a["num_seqs"], a["max_new"], a["kc"], a["vc"], a["kv_sb"],
+                                 a["kv_sh"], a["kv_st"], a["max_ctx"], a["hkv"], a["d"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(kn=None), -1, "null"),
+    (dict(pos=None), -1, "null"),
+    (dict(kc=40), -1, "aligned"),
+    (dict(cu=6), -1, "aligned"),
+    (dict(n_st=100), -1, "multiples of 8"),
+    (dict(hkv=0), -1, "positive"),
+    (dict(d=96), -2, "head_dim"),
+    (dict(max_new=-1), -1, ">= 0"),
+    (dict(vc=48), -1, "alias"),
+])
+def test_kv_append_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _kv_append(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_kv_append_empty_work_is_a_noop():
+    assert _kv_append(num_seqs=0, kn=None)[0] == 0
+    assert _kv_append(max_new=0)[0] == 0
+
+
 def _merge(**kw):
     a = dict(po=4, pm=4, pd=4, batch=2, hq=8, ns=4, d=64, o=16, o_sb=512, o_sh=64, lse=None)
     a.update(kw)

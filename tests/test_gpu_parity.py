@@ -429,3 +429,58 @@ def test_prefill_chunked_with_equal_boundaries_is_bitwise_prefill():
     out_c, lse_c = _chunked_gpu(chunk)
     assert torch.equal(out_c.view(torch.int16), out_p.view(torch.int16))
     assert torch.equal(lse_c, lse_p)
+
+
+# ------------------------------------------------------------- KV-cache append --
+def _random_bits_cache(B, Hkv, max_ctx, D, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(-32768, 32768, (B, Hkv, max_ctx, D), generator=g,
+                         dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("Hkv,D", [(8, 64), (4, 128), (1, 64)])
+def test_kv_append_bitwise(Hkv, D):
+    """Counts around the kernel's token blocks (0 .. 1000), positions at the
+    cache start, in the middle and at its end (the overflow is dropped); the
+    caches start as random bits and every slot is compared bit for bit."""
+    counts = [0, 1, 31, 32, 33, 200, 1000, 70]
+    max_ctx = 1100
+    pos = [5, 0, 1000, 17, 1067, 300, 100, 1090]      # request 7: 10 of 70 fit
+    inp = wl.kv_append_inputs(counts, max_ctx, Hkv, D, seed=100 + Hkv + D, pos=pos)
+    kc = _random_bits_cache(len(counts), Hkv, max_ctx, D, seed=1)
+    vc = _random_bits_cache(len(counts), Hkv, max_ctx, D, seed=2)
+    k_ref, v_ref = oracle.kv_append(inp["k_new"], inp["v_new"], inp["cu_seqlens_new"],
+                                    inp["cache_pos"], kc, vc)
+    kd, vd = kc.to(DEV), vc.to(DEV)
+    sa.sink_attn_kv_append(inp["k_new"].to(DEV), inp["v_new"].to(DEV),
+                           inp["cu_seqlens_new"].to(DEV), inp["cache_pos"].to(DEV), kd, vd,
+                           max_new=max(counts))
+    torch.cuda.synchronize()
+    assert torch.equal(kd.cpu().view(torch.int16), k_ref.view(torch.int16))
+    assert torch.equal(vd.cpu().view(torch.int16), v_ref.view(torch.int16))
+
+
+def test_kv_append_from_a_fused_qkv_row():
+    """New rows read straight out of a fused [T, Hq + 2 Hkv, D] QKV tensor
+    (token stride (Hq + 2 Hkv) * D), into caches that are a slice of a larger
+    allocation (strided requests)."""
+    Hq, Hkv, D, max_ctx = 16, 4, 64, 300
+    counts = [40, 129, 7]
+    inp = wl.kv_append_inputs(counts, max_ctx, Hkv, D, seed=120)
+    T = sum(counts)
+    g = torch.Generator().manual_seed(121)
+    qkv = torch.randn(T, Hq + 2 * Hkv, D, generator=g).to(torch.bfloat16)
+    qkv[:, Hq:Hq + Hkv] = inp["k_new"]
+    qkv[:, Hq + Hkv:] = inp["v_new"]
+    big_k = _random_bits_cache(6, Hkv, max_ctx, D, seed=3)
+    big_v = _random_bits_cache(6, Hkv, max_ctx, D, seed=4)
+    kc, vc = big_k[::2], big_v[::2]                     # requests 2 cache rows apart
+    k_ref, v_ref = oracle.kv_append(inp["k_new"], inp["v_new"], inp["cu_seqlens_new"],
+                                    inp["cache_pos"], kc, vc)
+    qd, bkd, bvd = qkv.to(DEV), big_k.to(DEV), big_v.to(DEV)
+    sa.sink_attn_kv_append(qd[:, Hq:Hq + Hkv], qd[:, Hq + Hkv:], inp["cu_seqlens_new"].to(DEV),
+                           inp["cache_pos"].to(DEV), bkd[::2], bvd[::2], max_new=max(counts))
+    torch.cuda.synchronize()
+    assert torch.equal(bkd.cpu()[::2].view(torch.int16), k_ref.view(torch.int16))
+    assert torch.equal(bvd.cpu()[::2].view(torch.int16), v_ref.view(torch.int16))
+    assert torch.equal(bkd.cpu()[1::2].view(torch.int16), big_k[1::2].view(torch.int16))
