@@ -234,6 +234,77 @@ def multi_decode_measurement(dev, stream, reps: int):
             "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def hbm_read_reference(dev, stream, reps: int = 10):
+    """GB/s of a plain streaming-read kernel (libhbmprobe.so, built beside the
+    library): 4 GiB read once per launch, each workgroup a contiguous slice,
+    non-temporal 16-byte loads."""
+    import ctypes
+    path = os.path.join(ROOT, "gqa_attention_sinks_prefill_amd", "libhbmprobe.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: run `python -m gqa_attention_sinks_prefill_amd.build_native`")
+    lib = ctypes.CDLL(path)
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    nbytes, blocks = 4 << 30, 8192
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.zeros(blocks, dtype=torch.int32, device=dev)
+    sp = stream.cuda_stream
+    run = lambda: lib.hbm_read_probe(buf.data_ptr(), nbytes, blocks, out.data_ptr(), sp)
+    for _ in range(3):
+        if run() != 0:
+            raise RuntimeError("hbm_read_probe failed")
+    torch.cuda.synchronize()
+    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+         for _ in range(reps)]
+    for a, b in e:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
+    del buf
+    return {"kernel": "hbm_read_probe (contiguous slices, non-temporal 16-byte loads, 8192 x 256 threads)",
+            "bytes": nbytes, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s"}
+
+
+def ragged_decode_measurement(dev, stream, batch: int, reps: int):
+    """KV GB/s of split decode + merge over contexts U[1024, 32768] (64 / 8 heads,
+    d 64, 1024-token chunks); B = 1 and 8 are launch / latency bound."""
+    cfg = wl.ragged_decode(batch)
+    d = wl.decode_inputs(cfg)
+    q, kc, vc = d["q"].to(dev), d["k_cache"].to(dev), d["v_cache"].to(dev)
+    lens, sinks = d["seq_lens"].to(dev), d["sinks"].to(dev)
+    B, Hq, D = q.shape
+    ns = cfg.num_splits
+    po = torch.empty(B, Hq, ns, D, device=dev)
+    pm = torch.empty(B, Hq, ns, device=dev)
+    pd = torch.empty(B, Hq, ns, device=dev)
+    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    run = lambda: sa.sink_attn_decode(q, kc, vc, lens, sinks, cfg.split_size, ns,
+                                      scale=cfg.scale, out=out, partials=(po, pm, pd),
+                                      stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+         for _ in range(reps)]
+    for a, b in e:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
+    kv = wl.decode_kv_bytes(d["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
+    gbs = kv / (ms * 1e-3) / 1e9
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
+            "metric": "decode KV GB/s (split + merge)", "mean_ms": round(ms, 4),
+            "algorithmic_bytes_per_step": kv,
+            "latency_bound": batch < 32,
+            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def copy_calibration(dev, reps: int):
     """A plain device-to-device copy of 1 GiB: reads and writes exactly 2^30
     bytes each, the reference that scales the HBM byte counters."""
@@ -372,6 +443,12 @@ def main():
                         chunked_prefill_measurement(dev, stream, max(3, args.steps // 2)),
                         multi_decode_measurement(dev, stream, max(3, args.steps // 2)),
                         kv_append_measurement(dev, stream, max(3, args.steps // 2))]
+        res["extra"] += [ragged_decode_measurement(dev, stream, b, max(3, args.steps // 4))
+                         for b in wl.RAGGED_BATCHES]
+    if run_d and not args.no_extra:
+        ref = hbm_read_reference(dev, stream)
+        res["hbm_read_reference"] = ref
+        res["decode"]["frac_of_measured_read"] = round(split_gbs / ref["value"], 4)
     if args.only != "all":
         res["note"] = f"--only {args.only}: the other part of the step was not launched"
     if args.cpu_seconds > 0 and run_p:

@@ -190,6 +190,8 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
   a.q_len = q_len;
   a.ncols = static_cast<int32_t>(ncols);
   a.head_slices = static_cast<int32_t>(head_slices);
+  a.batch = batch;
+  a.num_units = static_cast<int32_t>(num_blocks);
   a.split_size = split_size;
   a.num_splits = num_splits;
   a.scale_log2 = scale * 1.4426950408889634f;

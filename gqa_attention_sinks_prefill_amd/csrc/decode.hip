@@ -54,29 +54,33 @@ template <int DC> __device__ __forceinline__ int dv_swz(int row) {
   return 2 * ((row / (16 / DC)) & (DC / 2 - 1));
 }
 
-// head_dim 64 with up to 2 column blocks: two workgroups per CU (64 KB of LDS
-// each), so 2 waves / SIMD; wider blocks and head_dim 128 need the registers
-// of 1 wave / SIMD.
+// LDS of one decode workgroup: the waves' V double buffers, later reused for
+// the final merge of the four waves' states (m, l and o of every column, fp32).
 template <int D, int CB>
-__global__ __launch_bounds__(kThreads, (D == 64 && CB <= 2) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
+constexpr int decode_smem_elems() {
+  return 4 * 2 * kSub * D > 2 * (8 * 16 * CB + 4 * D * 16 * CB) ? 4 * 2 * kSub * D
+                                                                  : 2 * (8 * 16 * CB + 4 * D * 16 * CB);
+}
+
+// One work unit: chunk c of request b, KV head g, column slice hs.
+template <int D, int CB>
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint16_t* smem) {
   constexpr int DC = D / 8;                  // 16-byte chunks per row
   constexpr int TILE = kSub * D;             // elements of one V sub-tile
   constexpr int NDMA = kSub * DC / 64;       // DMA instructions per V sub-tile
   constexpr int NCC = D / 32;                // 32-d chunks of a K fragment row
   constexpr int NC = 16 * CB;                // columns of a workgroup
-  // LDS: the waves' V double buffers, later reused for the final merge of
-  // the four waves' states (m, l and o of every column, fp32).
   constexpr int kMergeFloats = 8 * NC + 4 * D * NC;
-  constexpr int kSmemElems = 4 * 2 * TILE > 2 * kMergeFloats ? 4 * 2 * TILE : 2 * kMergeFloats;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kSmemElems];
+  constexpr int kSmemElems = decode_smem_elems<D, CB>();
 
-  int unit = blockIdx.x;
-  const int c = unit % a.num_splits;
-  unit /= a.num_splits;
+  // units run chunk-major, so that the units one workgroup strides over mix
+  // chunks near the start of the requests with (often empty) later ones
   const int hs = unit % a.head_slices;
   unit /= a.head_slices;
   const int g = unit % a.num_kv_heads;
-  const int b = unit / a.num_kv_heads;
+  unit /= a.num_kv_heads;
+  const int b = unit % a.batch;
+  const int c = unit / a.batch;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,6 +96,23 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CB <= 2) ? 2 : 1) void decode
   const int n_sub = (n + kSub - 1) / kSub;
   // keys of this chunk visible to every column
   const int n_all = min(n, len - (a.q_len - 1) - lo);
+
+  // A chunk past the request's end without the sink (ragged batches have many)
+  // has the state (o, m, d) = (0, -inf, 0): write it and leave.
+  if (n == 0 && c != 0) {
+    for (int item = tid; item < nx * D; item += kThreads) {
+      const int x = x0 + item / D, d = item % D;
+      const int64_t row =
+          (((int64_t)b * a.q_len + x / a.group) * a.num_q_heads + g * a.group + x % a.group) *
+              a.num_splits + c;
+      a.part_o[row * D + d] = 0.f;
+      if (d == 0) {
+        a.part_m[row] = -INFINITY;
+        a.part_d[row] = 0.f;
+      }
+    }
+    return;
+  }
 
   // Per column block: Q^T fragments (column = (new token, head), k = d), the
   // keys of this chunk the lane's column sees, and the softmax state.  The
@@ -314,6 +335,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 && CB <= 2) ? 2 : 1) void decode
   }
 }
 
+// Workgroups stride over the work units (a ragged batch has many empty chunks;
+// launching a workgroup for each made the dispatcher, not HBM, the limit).  head_dim 64 with up to 2 column blocks: two workgroups per
+// CU (64 KB of LDS each), so 2 waves / SIMD; wider blocks and head_dim 128
+// need the registers of 1 wave / SIMD.
+template <int D, int CB>
+__global__ __launch_bounds__(kThreads, (D == 64 && CB <= 2) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[decode_smem_elems<D, CB>()];
+  for (int unit = blockIdx.x; unit < a.num_units; unit += gridDim.x) {
+    decode_unit<D, CB>(a, unit, smem);
+    __syncthreads();                 // the next unit's copies reuse the LDS just read
+  }
+}
+
 // Wave-wide reductions (64 lanes) for the merge.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -402,10 +436,19 @@ int decode_column_blocks(int ncols, int head_dim) {
   return need <= 1 ? 1 : (need <= 2 ? 2 : most);
 }
 
+constexpr int kComputeUnits = 256;             // MI355X
+
 template <int D>
-hipError_t launch_decode_d(const DecodeArgs& a, int64_t num_blocks, hipStream_t stream) {
-  const dim3 grid((unsigned)num_blocks), block(kThreads);
-  switch (decode_column_blocks(a.ncols, D)) {
+hipError_t launch_decode_d(const DecodeArgs& a, int64_t num_units, hipStream_t stream) {
+  const int cb = decode_column_blocks(a.ncols, D);
+  // Up to 8 workgroups per resident slot, one unit each; beyond that a fixed
+  // grid of an odd count strides over the units, so that the units of one
+  // workgroup come from different requests (the hardware then balances
+  // whole workgroups as slots free up).
+  const int64_t resident = (int64_t)kComputeUnits * ((D == 64 && cb <= 2) ? 2 : 1);
+  const int64_t most = 8 * resident;
+  const dim3 grid((unsigned)(num_units <= most ? num_units : most - 1)), block(kThreads);
+  switch (cb) {
     case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, block, 0, stream, a); break;
     default:

@@ -44,7 +44,9 @@ struct DecodeArgs {
   int32_t group;          // query heads per KV head
   int32_t q_len;          // new tokens per request (1 for plain decode)
   int32_t ncols;          // q_len * group columns: (new token, query head)
-  int32_t head_slices;    // ceil(ncols / (16 * column blocks)): workgroups per (b, g, chunk)
+  int32_t head_slices;    // ceil(ncols / (16 * column blocks)): units per (b, g, chunk)
+  int32_t batch;
+  int32_t num_units;      // batch * num_kv_heads * head_slices * num_splits
   int32_t split_size;
   int32_t num_splits;
   float scale_log2;
