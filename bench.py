@@ -19,6 +19,13 @@ split + merge duration.  `roofline` compares the prefill kernel with the
 bf16 dense MFMA peak, `decode.roofline` the decode split kernel with the HBM
 peak.  `cpu_baseline` times the fp64 CPU oracle on a bounded random sample
 of prefill rows on this host, scaled to TFLOP/s.
+
+After the timed steps (not part of them): `hbm_read_reference` times a plain
+streaming-read kernel (libhbmprobe.so) and `decode.frac_of_measured_read`
+relates the decode to it; `extra` holds the other workloads' lines -- the
+head_dim 128 varlen prefill, chunked prefill, multi-token decode, KV-cache
+append and the ragged long-context decode at B = 1, 8, 32, 128 (B < 32 is
+launch / latency bound and flagged so).
 """
 from __future__ import annotations
 
