@@ -159,6 +159,9 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
   if (!stride_ok(q_stride_b) || !stride_ok(q_stride_tok) || !stride_ok(q_stride_head) ||
       !stride_ok(kv_stride_b) || !stride_ok(kv_stride_head) || !stride_ok(kv_stride_tok))
     return fail(SINK_ATTN_EINVAL, "strides must be non-negative multiples of 8 elements");
+  // a chunk of one head is addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(split_size) * kv_stride_tok * 2 > 0x7fffffffLL)
+    return fail(SINK_ATTN_EUNSUPPORTED, "split_size * kv_stride_tok spans more than 2 GiB");
 
   const int group = num_q_heads / num_kv_heads;
   const int64_t ncols = static_cast<int64_t>(q_len) * group;
@@ -191,7 +194,6 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
   a.ncols = static_cast<int32_t>(ncols);
   a.head_slices = static_cast<int32_t>(head_slices);
   a.batch = batch;
-  a.num_units = static_cast<int32_t>(num_blocks);
   a.split_size = split_size;
   a.num_splits = num_splits;
   a.scale_log2 = scale * 1.4426950408889634f;

@@ -8,15 +8,15 @@
 // the tokens of one head contiguous); section "Decoders": decode is bound by
 // memory traffic, so the kernel is built to stream the cache once.
 //
-// decode_split_kernel: one workgroup (4 waves) per (request b, KV head g,
-// slice of 16*CB columns, chunk c).  A column is one (new token t, query head of g)
+// decode_split_kernel: one workgroup of W = 1, 2 or 4 waves per (request b, KV
+// head g, slice of 16*CB columns, chunk c).  A column is one (new token t, query head of g)
 // pair: one new token per request for plain decode, q_len of them for the
 // multi-token decode of speculative / MTP verification ("GPT-OSS on day 0",
 // section "Internal inference engine"; "Hosting Qwen on Blackwell", section
 // "Decoders"), where new token t -- already in the cache, whose last q_len
 // tokens are the new ones -- sees the cache up to its own position.  The K/V
 // of the chunk are read exactly once and serve every column.  The chunk is cut
-// into 64-key sub-tiles; wave w takes sub-tiles w, w+4, w+8, ... and runs its
+// into 64-key sub-tiles; wave w takes sub-tiles w, w+W, w+2W, ... and runs its
 // own pipeline with no workgroup barrier until the final merge:
 //   * K of the next sub-tile is loaded HBM -> registers and V of the next
 //     sub-tile is copied HBM -> LDS (buffer->LDS DMA into the wave's double
@@ -31,8 +31,11 @@
 //     column's position are masked in the last sub-tiles;
 //   * O^T += V^T P^T on the same MFMA: P^T comes straight from the S^T
 //     accumulators, V^T from the row-major V tile via the transposing LDS read.
-// At the end the 4 waves' states are merged through LDS and the chunk's
+// At the end the W waves' states are merged through LDS (W > 1) and the chunk's
 // (o / d, m, d) is written in fp32.  Only wave 0 of chunk 0 seeds the sink.
+// W trades the merge across waves against parallelism inside a chunk: four
+// waves per chunk for one light column block; one wave per chunk, writing its
+// state directly, for heavier math when the chunks alone fill the SIMDs.
 // merge_kernel: one wave per (b, h) row, lane = d; log-sum-exp weighted sum of
 // the chunk states, rounded to bf16.
 #include "device_common.h"
@@ -42,7 +45,7 @@ namespace sinkattn {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;                 // merge kernel
 constexpr int kSub = 64;                      // keys per sub-tile
 
 // Chunk swizzle of the row-major V sub-tile (DC 16-byte chunks per row).  The
@@ -54,27 +57,38 @@ template <int DC> __device__ __forceinline__ int dv_swz(int row) {
   return 2 * ((row / (16 / DC)) & (DC / 2 - 1));
 }
 
-// LDS of one decode workgroup: the waves' V double buffers, later reused for
-// the final merge of the four waves' states (m, l and o of every column, fp32).
-template <int D, int CB>
-constexpr int decode_smem_elems() {
-  return 4 * 2 * kSub * D > 2 * (8 * 16 * CB + 4 * D * 16 * CB) ? 4 * 2 * kSub * D
-                                                                  : 2 * (8 * 16 * CB + 4 * D * 16 * CB);
+// fp32 values of the final merge of W waves' states: m and l of every column,
+// then o (none for a single wave, which writes its state directly).
+template <int D, int CB, int W>
+constexpr int decode_merge_floats() {
+  return W == 1 ? 0 : 2 * W * 16 * CB + W * D * 16 * CB;
+}
+// LDS of one decode workgroup (16-bit elements): two arrays of the waves' V
+// sub-tiles (even and odd sub-tiles), the first of them later reused for the
+// merge.  Two arrays rather than one with two halves: the compiler can then
+// see that a copy into one never aliases reads of the other, and does not make
+// the reads of sub-tile st wait for the copy of st + 1.
+template <int D, int CB, int W>
+constexpr int decode_lds0_elems() {
+  return W * kSub * D > 2 * decode_merge_floats<D, CB, W>() ? W * kSub * D
+                                                             : 2 * decode_merge_floats<D, CB, W>();
 }
 
-// One work unit: chunk c of request b, KV head g, column slice hs.
-template <int D, int CB>
-__device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint16_t* smem) {
+// One work unit: chunk c of request b, KV head g, column slice hs, on W waves.
+template <int D, int CB, int W>
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint16_t* v_lds0,
+                                            uint16_t* v_lds1) {
   constexpr int DC = D / 8;                  // 16-byte chunks per row
   constexpr int TILE = kSub * D;             // elements of one V sub-tile
   constexpr int NDMA = kSub * DC / 64;       // DMA instructions per V sub-tile
   constexpr int NCC = D / 32;                // 32-d chunks of a K fragment row
   constexpr int NC = 16 * CB;                // columns of a workgroup
-  constexpr int kMergeFloats = 8 * NC + 4 * D * NC;
-  constexpr int kSmemElems = decode_smem_elems<D, CB>();
+  constexpr int kMergeFloats = decode_merge_floats<D, CB, W>();
+  constexpr int kLds0Elems = decode_lds0_elems<D, CB, W>();
+  constexpr int kBlock = 64 * W;
 
-  // units run chunk-major, so that the units one workgroup strides over mix
-  // chunks near the start of the requests with (often empty) later ones
+  // units run chunk-major: the (often empty) late chunks of a ragged batch
+  // come last, where their workgroups leave at once
   const int hs = unit % a.head_slices;
   unit /= a.head_slices;
   const int g = unit % a.num_kv_heads;
@@ -96,15 +110,18 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
   const int n_sub = (n + kSub - 1) / kSub;
   // keys of this chunk visible to every column
   const int n_all = min(n, len - (a.q_len - 1) - lo);
+  // row of column x in the partial outputs
+  auto out_row = [&](int x) {
+    return (((int64_t)b * a.q_len + x / a.group) * a.num_q_heads + g * a.group + x % a.group) *
+               a.num_splits + c;
+  };
 
   // A chunk past the request's end without the sink (ragged batches have many)
   // has the state (o, m, d) = (0, -inf, 0): write it and leave.
   if (n == 0 && c != 0) {
-    for (int item = tid; item < nx * D; item += kThreads) {
-      const int x = x0 + item / D, d = item % D;
-      const int64_t row =
-          (((int64_t)b * a.q_len + x / a.group) * a.num_q_heads + g * a.group + x % a.group) *
-              a.num_splits + c;
+    for (int item = tid; item < nx * D; item += kBlock) {
+      const int64_t row = out_row(x0 + item / D);
+      const int d = item % D;
       a.part_o[row * D + d] = 0.f;
       if (d == 0) {
         a.part_m[row] = -INFINITY;
@@ -115,7 +132,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
   }
 
   // Per column block: Q^T fragments (column = (new token, head), k = d), the
-  // keys of this chunk the lane's column sees, and the softmax state.  The
+  // keys of the run the lane's column sees, and the softmax state.  The
   // sink seeds wave 0 of chunk 0 only, counted once (row group 0).
   const bool seeded = (c == 0) && (wave == 0);
   u32x4_t qf[CB][NCC];
@@ -168,7 +185,6 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
     const int cl = 2 * db + ((col & 3) >> 1);
     v_roff[db] = row * D + ((cl ^ dv_swz<DC>(row)) * 8) + 4 * (col & 1);
   }
-  uint16_t* vbuf = smem + wave * 2 * TILE;
 
   auto load_k = [&](int st, u32x4_t (&kf)[4][NCC]) {
     const int off = st * kSub * st2;
@@ -177,14 +193,16 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc) kf[kb][cc] = buffer_load16<kNonTemporal>(krs, k_off[cc] + kb * 16 * st2 + off);
   };
-  auto dma_v = [&](int st, int buf) {
+  // Buffer numbers are compile-time constants (std::integral_constant).
+  auto dma_v = [&](int st, auto buf) {
     const int off = st * kSub * st2;
+    uint16_t* dst = (decltype(buf)::value ? v_lds1 : v_lds0) + wave * TILE;
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) buffer_load16_lds<kNonTemporal>(vrs, vbuf + buf * TILE + i * 512, v_goff[i] + off);
+    for (int i = 0; i < NDMA; ++i) buffer_load16_lds<kNonTemporal>(vrs, dst + i * 512, v_goff[i] + off);
   };
   // One 64-key sub-tile: every K operand and every V^T operand feeds the CB
   // column blocks' MFMAs.
-  auto compute = [&](int st, int buf, const u32x4_t (&kf)[4][NCC]) {
+  auto compute = [&](int st, auto buf, const u32x4_t (&kf)[4][NCC]) {
     f32x4_t s[CB][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -242,7 +260,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
         pf[cb][j][3] = pack_bf16x2(sc[2 * j + 1][2], sc[2 * j + 1][3]);
       }
     }
-    const uint16_t* vt = vbuf + buf * TILE;
+    const uint16_t* vt = (decltype(buf)::value ? v_lds1 : v_lds0) + wave * TILE;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
@@ -257,95 +275,109 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
     }
   };
 
-  // ---- per-wave pipeline over sub-tiles wave, wave+4, ... --------------------
+  // ---- per-wave pipeline over sub-tiles wave, wave+W, ... --------------------
   // At the top of each pass this wave's copies for sub-tile st are complete;
-  // the copies for st + 4 are then issued and run during st's math.  Two
+  // the copies for st + W are then issued and run during st's math.  Two
   // passes per loop trip so the K register sets swap roles without copies.
+  const std::integral_constant<int, 0> even{};
+  const std::integral_constant<int, 1> odd{};
   u32x4_t ka[4][NCC], kb2[4][NCC];
   int st = wave;
   if (st < n_sub) {
     load_k(st, ka);
-    dma_v(st, 0);
+    dma_v(st, even);
   }
-  int it = 0;
+  auto pass = [&](auto buf, const u32x4_t (&kcur)[4][NCC], u32x4_t (&knext)[4][NCC]) {
+    wait_vmem();
+    if (st + W < n_sub) {
+      load_k(st + W, knext);
+      dma_v(st + W, std::integral_constant<int, 1 - decltype(buf)::value>{});
+    }
+    compute(st, buf, kcur);
+    st += W;
+  };
   while (st < n_sub) {
-    wait_vmem();
-    if (st + 4 < n_sub) {
-      load_k(st + 4, kb2);
-      dma_v(st + 4, (it + 1) & 1);
-    }
-    compute(st, it & 1, ka);
-    st += 4;
-    ++it;
+    pass(even, ka, kb2);
     if (st >= n_sub) break;
-    wait_vmem();
-    if (st + 4 < n_sub) {
-      load_k(st + 4, ka);
-      dma_v(st + 4, (it + 1) & 1);
-    }
-    compute(st, it & 1, kb2);
-    st += 4;
-    ++it;
+    pass(odd, kb2, ka);
   }
 
-  // ---- merge the four waves' states through LDS ------------------------------
+  if constexpr (W == 1) {
+    // ---- one wave: its state is the chunk's ---------------------------------
+    // Streamed out (non-temporal): with one wave per chunk the waves write
+    // 2-4x more state per byte read than the merged form, and as plain
+    // stores under the saturating read stream they were acknowledged so late
+    // that they held up the waves' later waits (q_len 4: 12% slower).
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) l[cb] = pair32_sum(pair16_sum(l[cb]));
-  __syncthreads();                    // every wave is done with its V buffers
-  static_assert(2 * kMergeFloats <= kSmemElems, "merge buffers must fit in LDS");
-  float* red = reinterpret_cast<float*>(smem);
-  float* red_m = red;                 // [4][NC]
-  float* red_l = red + 4 * NC;        // [4][NC]
-  float* red_o = red + 8 * NC;        // [4][D][NC]
+    for (int cb = 0; cb < CB; ++cb) {
+      const float lt = pair32_sum(pair16_sum(l[cb]));
+      if (cb * 16 + col >= nx) continue;
+      const int64_t row = out_row(x0 + cb * 16 + col);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      float* op = a.part_o + row * D + 4 * lgrp;
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const int xl = cb * 16 + col;
-    if (lgrp == 0) {
-      red_m[wave * NC + xl] = m[cb];
-      red_l[wave * NC + xl] = l[cb];
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_nt(op + 16 * db + i, acc[cb][db][i] * inv);
+      if (lgrp == 0) {
+        store_nt(a.part_m + row, lt > 0.f ? m[cb] * kLn2 : -INFINITY);
+        store_nt(a.part_d + row, lt);
+      }
     }
+  } else {
+    // ---- merge the W waves' states through LDS ------------------------------
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
+    for (int cb = 0; cb < CB; ++cb) l[cb] = pair32_sum(pair16_sum(l[cb]));
+    __syncthreads();                  // every wave is done with its V buffers
+    static_assert(2 * kMergeFloats <= kLds0Elems, "merge buffers must fit in LDS");
+    float* red = reinterpret_cast<float*>(v_lds0);
+    float* red_m = red;               // [W][NC]
+    float* red_l = red + W * NC;      // [W][NC]
+    float* red_o = red + 2 * W * NC;  // [W][D][NC]
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red_o[(wave * D + db * 16 + 4 * lgrp + i) * NC + xl] = acc[cb][db][i];
-  }
-  __syncthreads();
+    for (int cb = 0; cb < CB; ++cb) {
+      const int xl = cb * 16 + col;
+      if (lgrp == 0) {
+        red_m[wave * NC + xl] = m[cb];
+        red_l[wave * NC + xl] = l[cb];
+      }
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red_o[(wave * D + db * 16 + 4 * lgrp + i) * NC + xl] = acc[cb][db][i];
+    }
+    __syncthreads();
 
-  for (int item = tid; item < nx * D; item += kThreads) {
-    const int xl = item / D, d = item % D;
-    const int x = x0 + xl;
-    float M = -__FLT_MAX__;
+    for (int item = tid; item < nx * D; item += kBlock) {
+      const int xl = item / D, d = item % D;
+      float M = -__FLT_MAX__;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w * NC + xl]);
-    float wsum = 0.f, o = 0.f;
+      for (int w = 0; w < W; ++w) M = fmaxf(M, red_m[w * NC + xl]);
+      float wsum = 0.f, o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = fast_exp2(red_m[w * NC + xl] - M);
-      wsum += red_l[w * NC + xl] * f;
-      o += red_o[(w * D + d) * NC + xl] * f;
-    }
-    const int64_t row =
-        (((int64_t)b * a.q_len + x / a.group) * a.num_q_heads + g * a.group + x % a.group) *
-            a.num_splits + c;
-    a.part_o[row * D + d] = wsum > 0.f ? o / wsum : 0.f;
-    if (d == 0) {
-      a.part_m[row] = wsum > 0.f ? M * kLn2 : -INFINITY;
-      a.part_d[row] = wsum;
+      for (int w = 0; w < W; ++w) {
+        const float f = fast_exp2(red_m[w * NC + xl] - M);
+        wsum += red_l[w * NC + xl] * f;
+        o += red_o[(w * D + d) * NC + xl] * f;
+      }
+      const int64_t row = out_row(x0 + xl);
+      a.part_o[row * D + d] = wsum > 0.f ? o / wsum : 0.f;
+      if (d == 0) {
+        a.part_m[row] = wsum > 0.f ? M * kLn2 : -INFINITY;
+        a.part_d[row] = wsum;
+      }
     }
   }
 }
 
-// Workgroups stride over the work units (a ragged batch has many empty chunks;
-// launching a workgroup for each made the dispatcher, not HBM, the limit).  head_dim 64 with up to 2 column blocks: two workgroups per
-// CU (64 KB of LDS each), so 2 waves / SIMD; wider blocks and head_dim 128
-// need the registers of 1 wave / SIMD.
-template <int D, int CB>
-__global__ __launch_bounds__(kThreads, (D == 64 && CB <= 2) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[decode_smem_elems<D, CB>()];
-  for (int unit = blockIdx.x; unit < a.num_units; unit += gridDim.x) {
-    decode_unit<D, CB>(a, unit, smem);
-    __syncthreads();                 // the next unit's copies reuse the LDS just read
-  }
+// One workgroup per unit.  head_dim 64 with up to 2 column blocks runs 2 waves
+// per SIMD (16 KB of LDS per wave); wider blocks and head_dim 128 need the
+// registers of 1 wave per SIMD.
+template <int D, int CB, int W>
+__global__ __launch_bounds__(64 * W, (D == 64 && CB <= 2) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[decode_lds0_elems<D, CB, W>()];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[W * kSub * D];
+  decode_unit<D, CB, W>(a, blockIdx.x, v_lds0, v_lds1);
 }
 
 // Wave-wide reductions (64 lanes) for the merge.
@@ -438,24 +470,42 @@ int decode_column_blocks(int ncols, int head_dim) {
 
 constexpr int kComputeUnits = 256;             // MI355X
 
+int decode_waves_per_unit(int64_t num_units, int head_dim, int column_blocks) {
+  // head_dim 64 with one column block: little math per sub-tile, and four
+  // waves per chunk shorten each chunk's critical path, which ragged batches
+  // need (B = 8 / 32 contexts U[1024, 32768]: 9% / 5% faster than a wave per
+  // chunk; uniform 64 x 8192 contexts equal).  Heavier math (more column
+  // blocks, head_dim 128) makes the waves sharing a chunk wait for one another
+  // at the merge -- at 1 wave per SIMD that stalls the CU -- so there each wave
+  // takes a chunk of its own (q_len 4 / 8 and head_dim 128: 15% / 80% / 8%
+  // faster), unless that leaves SIMDs idle.
+  if (head_dim == 64 && column_blocks == 1) return 4;
+  const int64_t simds = (int64_t)kComputeUnits * 4;
+  return num_units >= simds ? 1 : (2 * num_units >= simds ? 2 : 4);
+}
+
+template <int D, int CB>
+hipError_t launch_decode_cb(const DecodeArgs& a, int64_t num_units, int waves, hipStream_t stream) {
+  const dim3 grid((unsigned)num_units);
+  switch (waves) {
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, CB, 1>), grid, dim3(64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, CB, 2>), grid, dim3(128), 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, CB, 4>), grid, dim3(256), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, int64_t num_units, hipStream_t stream) {
   const int cb = decode_column_blocks(a.ncols, D);
-  // Up to 8 workgroups per resident slot, one unit each; beyond that a fixed
-  // grid of an odd count strides over the units, so that the units of one
-  // workgroup come from different requests (the hardware then balances
-  // whole workgroups as slots free up).
-  const int64_t resident = (int64_t)kComputeUnits * ((D == 64 && cb <= 2) ? 2 : 1);
-  const int64_t most = 8 * resident;
-  const dim3 grid((unsigned)(num_units <= most ? num_units : most - 1)), block(kThreads);
+  const int waves = decode_waves_per_unit(num_units, D, cb);
   switch (cb) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<D, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, 2>), grid, block, 0, stream, a); break;
+    case 1: return launch_decode_cb<D, 1>(a, num_units, waves, stream);
+    case 2: return launch_decode_cb<D, 2>(a, num_units, waves, stream);
     default:
-      if constexpr (D == 64) hipLaunchKernelGGL((decode_split_kernel<D, 4>), grid, block, 0, stream, a);
-      break;
+      if constexpr (D == 64) return launch_decode_cb<D, 4>(a, num_units, waves, stream);
+      return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,

@@ -116,14 +116,20 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2_t, r);
 }
 
-// max of three floats in one instruction (v_max3_f32)
 // acc + the two bf16 halves of `packed` (v_dot2 with a pair of ones).
 __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
                                          __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
 }
+// max of three floats in one instruction (v_max3_f32)
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Store of a result no kernel of this launch reads back (the "nt" bit):
+// streamed out rather than kept in the cache.  Under a saturating read
+// stream, plain stores of the split-decode states were acknowledged so late
+// that the waves' waits for their next copies stalled on them.
+__device__ __forceinline__ void store_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
 
 
 }  // namespace sinkattn

@@ -46,7 +46,6 @@ struct DecodeArgs {
   int32_t ncols;          // q_len * group columns: (new token, query head)
   int32_t head_slices;    // ceil(ncols / (16 * column blocks)): units per (b, g, chunk)
   int32_t batch;
-  int32_t num_units;      // batch * num_kv_heads * head_slices * num_splits
   int32_t split_size;
   int32_t num_splits;
   float scale_log2;
@@ -86,6 +85,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int64_t num_blocks
                           hipStream_t stream);
 // Blocks of 16 columns one decode workgroup serves (1, 2, or up to 4 for head_dim 64).
 int decode_column_blocks(int ncols, int head_dim);
+// Waves (1, 2 or 4) that share one decode work unit.
+int decode_waves_per_unit(int64_t num_units, int head_dim, int column_blocks);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,
                                hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

@@ -131,7 +131,8 @@ int sink_attn_prefill_chunked(const void* q, int64_t q_stride_tok, int64_t q_str
  *       b at base + b*kv_stride_b + g*kv_stride_head + j*kv_stride_tok (the
  *       two caches share the strides).
  *   seq_lens [B] int32, device.  Precondition: 0 <= seq_lens[b] <= max_ctx.
- *   split_size: tokens per chunk, a positive multiple of 64.
+ *   split_size: tokens per chunk, a positive multiple of 64, with
+ *       split_size * kv_stride_tok * 2 < 2^31 (else SINK_ATTN_EUNSUPPORTED).
  *   num_splits: chunks per request; num_splits * split_size >= max_ctx.
  *   Outputs, for row (b, h) and chunk c = 0 .. num_splits-1, chunk c covering
  *   tokens [c*split_size, min((c+1)*split_size, seq_lens[b])):

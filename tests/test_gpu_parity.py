@@ -373,6 +373,62 @@ def test_decode_multi_full_config_sampled_rows():
                      what="multi decode full config lse")
 
 
+_EDGE_LENS = [0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 447, 448, 511, 512]
+
+
+@pytest.mark.parametrize("B,Hkv,D,q_len,split", [
+    (128, 8, 64, 1, 64),      # one column block: four waves per chunk
+    (128, 8, 64, 3, 64),      # 24 columns (two blocks), 8192 chunks: a wave per chunk
+    (24, 8, 64, 3, 128),      # two blocks, 768 chunks: two waves per chunk
+    (32, 8, 64, 8, 128),      # 64 columns (four blocks), 1024 chunks: a wave per chunk
+    (64, 8, 128, 1, 128),     # head_dim 128, 2048 chunks: a wave per chunk
+])
+def test_decode_work_splits_edge_lengths(B, Hkv, D, q_len, split):
+    """Each way a chunk is shared by waves (one, two or four per chunk), at
+    launches big enough to pick it, with lengths on and around sub-tile and
+    chunk edges, zero included; every chunk state is checked (empty chunks
+    exactly (0, -inf, 0)), not only the merged output."""
+    lens = [_EDGE_LENS[(7 * i) % len(_EDGE_LENS)] for i in range(B)]
+    inp = _multi_cfg(lens, q_len, 64, Hkv, D, seed=90 + q_len + D + split, split=split,
+                     max_ctx=512, edges={0: float("-inf"), 63: 20.0})
+    if inp["q"].dim() == 3:
+        inp = dict(inp, q=inp["q"].unsqueeze(1))
+    q = inp["q"].to(DEV)
+    kc, vc = inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    ns = 512 // split
+    po = torch.full((B, q_len, 64, ns, D), float("nan"), device=DEV)
+    pm = torch.full((B, q_len, 64, ns), float("nan"), device=DEV)
+    pd = torch.full((B, q_len, 64, ns), float("nan"), device=DEV)
+    out = torch.full((B, q_len, 64, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, q_len, 64), float("nan"), device=DEV)
+    sa.sink_attn_decode_multi(q, kc, vc, inp["seq_lens"].to(DEV), inp["sinks"].to(DEV), split,
+                              ns, out=out, lse=lse, partials=(po, pm, pd))
+    torch.cuda.synchronize()
+    o_ref, lse_ref, _ = oracle.decode_multi(inp["q"], inp["k_cache"], inp["v_cache"],
+                                            inp["seq_lens"], inp["sinks"])
+    what = f"decode B={B} D={D} q_len={q_len} split={split}"
+    assert_close(out.reshape(-1, D), o_ref, what=what)
+    assert_lse_close(lse.reshape(-1), lse_ref, what=f"{what} lse")
+    # the chunk states themselves (empty chunks exactly (0, -inf, 0))
+    po, pm, pd = po.cpu(), pm.cpu(), pd.cpu()
+    assert not torch.isnan(po).any() and not torch.isnan(pm).any() and not torch.isnan(pd).any()
+    for b, L in enumerate(lens):
+        first_empty = max(-(-L // split), 1)
+        assert torch.all(po[b, :, :, first_empty:] == 0)
+        assert torch.all(pm[b, :, :, first_empty:] == float("-inf"))
+        assert torch.all(pd[b, :, :, first_empty:] == 0)
+    if q_len == 1:
+        rows = [(b, h) for b in range(0, B, 5) for h in (0, 17, 63)]
+        o_c, m_c, d_c = oracle.chunk_states(inp["q"][:, 0], inp["k_cache"], inp["v_cache"],
+                                            inp["seq_lens"], inp["sinks"], split, ns, rows=rows)
+        idx = torch.tensor(rows)
+        assert_close(po[idx[:, 0], 0, idx[:, 1]], o_c, what=f"{what} chunk o")
+        g_m = pm[idx[:, 0], 0, idx[:, 1]].double().numpy()
+        g_d = pd[idx[:, 0], 0, idx[:, 1]].double().numpy()
+        np.testing.assert_allclose(g_m, m_c, rtol=0, atol=2e-3)
+        np.testing.assert_allclose(g_d, d_c, rtol=2e-3)
+
+
 # ------------------------------------------------------------ chunked prefill --
 def _chunked_gpu(inp, *, causal=True):
     q = inp["q"].to(DEV)
