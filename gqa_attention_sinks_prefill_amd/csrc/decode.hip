@@ -304,25 +304,37 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
 
   if constexpr (W == 1) {
     // ---- one wave: its state is the chunk's ---------------------------------
-    // Streamed out (non-temporal): with one wave per chunk the waves write
-    // 2-4x more state per byte read than the merged form, and as plain
-    // stores under the saturating read stream they were acknowledged so late
-    // that they held up the waves' later waits (q_len 4: 12% slower).
+    // Streamed out (non-temporal): as plain stores under the saturating read
+    // stream they were acknowledged so late that they held up the waves'
+    // later waits (q_len 4: 12% slower).
+    // o / d of every column goes through LDS ([column][d] fp32, 16-byte
+    // chunks XOR-swizzled by the column; the V buffers are free now) so that
+    // part_o is written in whole rows.  Each V array holds two column blocks.
+    static_assert(2 * 16 * D * 2 <= kSub * D, "two column blocks of o fit one V array");
+    __syncthreads();
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const float lt = pair32_sum(pair16_sum(l[cb]));
-      if (cb * 16 + col >= nx) continue;
-      const int64_t row = out_row(x0 + cb * 16 + col);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      float* op = a.part_o + row * D + 4 * lgrp;
+      float* stg = reinterpret_cast<float*>(cb < 2 ? v_lds0 : v_lds1) + (cb & 1) * 16 * D;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_nt(op + 16 * db + i, acc[cb][db][i] * inv);
-      if (lgrp == 0) {
+        *reinterpret_cast<f32x4_t*>(stg + col * D + 4 * ((4 * db + lgrp) ^ col)) = acc[cb][db] * inv;
+      if (lgrp == 0 && cb * 16 + col < nx) {
+        const int64_t row = out_row(x0 + cb * 16 + col);
         store_nt(a.part_m + row, lt > 0.f ? m[cb] * kLn2 : -INFINITY);
         store_nt(a.part_d + row, lt);
       }
+    }
+    __syncthreads();
+    for (int item = lane; item < nx * (D / 4); item += 64) {
+      const int xl = item / (D / 4), d4 = item % (D / 4);
+      const int cb = xl / 16, xc = xl % 16;
+      const float* stg = reinterpret_cast<const float*>(cb < 2 ? v_lds0 : v_lds1) + (cb & 1) * 16 * D;
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + xc * D + 4 * (d4 ^ xc));
+      float* op = a.part_o + out_row(x0 + xl) * D + 4 * d4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_nt(op + i, v[i]);
     }
   } else {
     // ---- merge the W waves' states through LDS ------------------------------
