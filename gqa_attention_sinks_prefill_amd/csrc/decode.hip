@@ -345,7 +345,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
     float* red = reinterpret_cast<float*>(v_lds0);
     float* red_m = red;               // [W][NC]
     float* red_l = red + W * NC;      // [W][NC]
-    float* red_o = red + 2 * W * NC;  // [W][D][NC]
+    float* red_o = red + 2 * W * NC;  // [W][NC][D], 16-byte chunks XOR-swizzled by column
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int xl = cb * 16 + col;
@@ -355,26 +355,31 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
       }
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red_o[(wave * D + db * 16 + 4 * lgrp + i) * NC + xl] = acc[cb][db][i];
+        *reinterpret_cast<f32x4_t*>(red_o + (wave * NC + xl) * D + 4 * ((4 * db + lgrp) ^ col)) =
+            acc[cb][db];
     }
     __syncthreads();
 
-    for (int item = tid; item < nx * D; item += kBlock) {
-      const int xl = item / D, d = item % D;
+    // four consecutive d of one column per thread: whole rows of part_o
+    for (int item = tid; item < nx * (D / 4); item += kBlock) {
+      const int xl = item / (D / 4), c4 = item % (D / 4);
       float M = -__FLT_MAX__;
 #pragma unroll
       for (int w = 0; w < W; ++w) M = fmaxf(M, red_m[w * NC + xl]);
-      float wsum = 0.f, o = 0.f;
+      float wsum = 0.f;
+      f32x4_t o = {};
 #pragma unroll
       for (int w = 0; w < W; ++w) {
         const float f = fast_exp2(red_m[w * NC + xl] - M);
         wsum += red_l[w * NC + xl] * f;
-        o += red_o[(w * D + d) * NC + xl] * f;
+        o += *reinterpret_cast<const f32x4_t*>(red_o + (w * NC + xl) * D + 4 * (c4 ^ (xl & 15))) * f;
       }
       const int64_t row = out_row(x0 + xl);
-      a.part_o[row * D + d] = wsum > 0.f ? o / wsum : 0.f;
-      if (d == 0) {
+      const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+      float* op = a.part_o + row * D + 4 * c4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) op[i] = o[i] * inv;
+      if (c4 == 0) {
         a.part_m[row] = wsum > 0.f ? M * kLn2 : -INFINITY;
         a.part_d[row] = wsum;
       }
