@@ -312,3 +312,150 @@ def kv_append(k_new, v_new, cu_seqlens_new, cache_pos, k_cache, v_cache):
                 kc[b, :, slot, :] = k_new[cu[b] + t]
                 vc[b, :, slot, :] = v_new[cu[b] + t]
     return kc, vc
+
+
+# ----------------------------------------------------------- FP8 KV cache --
+# The pages name FP8 only for weights; an FP8 KV cache is a plain extension
+# (the decode step is memory-bound, "Hosting Qwen on Blackwell", section
+# "Decoders").  Reading taken: the cache holds OCP FP8 E4M3 codes (1 sign,
+# 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+# subnormal; S.1111.111 is NaN; no infinities; largest finite 448), with one
+# fp32 scale per KV head: value = e4m3(code) * scale[g].  Attention is then
+# the same definition, evaluated on the dequantized values in float64.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """The real number an E4M3 code stands for, from the format's definition."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return float("nan")
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], np.float64)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """float32 values -> E4M3 codes: round to nearest, ties to the even
+    mantissa, magnitudes past 448 saturated to +-448, NaN -> 0x7F.
+
+    By brute force against the table of finite codes: the nearest value;
+    among equally near codes the one with an even mantissa, and between +0
+    and -0 the one with the sign of x.
+    """
+    x = np.asarray(x, np.float32).astype(np.float64)
+    codes = np.array([c for c in range(256) if not math.isnan(E4M3_TABLE[c])])
+    vals = E4M3_TABLE[codes]
+    odd = (codes & 1).astype(np.int64)
+    neg = (codes >> 7).astype(np.int64)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
+    for s in range(0, flat.size, 1 << 15):
+        v = flat[s:s + (1 << 15)]
+        nan = np.isnan(v)
+        vc = np.clip(np.where(nan, 0.0, v), -E4M3_MAX, E4M3_MAX)
+        dist = np.abs(vals[None, :] - vc[:, None])
+        tie = dist == dist.min(axis=1, keepdims=True)
+        sign_x = np.signbit(vc).astype(np.int64)
+        rank = np.where(tie, 2 * odd[None, :] + (neg[None, :] != sign_x[:, None]), 99)
+        c = codes[np.argmin(rank, axis=1)]
+        out[s:s + v.size] = np.where(nan, 0x7F, c)
+    return out.reshape(x.shape)
+
+
+def fp8_quantize(x, scale) -> np.ndarray:
+    """Quantize values for a cache with dequantization scale `scale` (any
+    shape broadcasting against x): code = e4m3_encode(fp32(x) * fp32(1 / scale)),
+    the reciprocal and the product each rounded to float32 (the form a kernel
+    evaluates)."""
+    inv = np.float32(1.0) / np.asarray(scale, np.float32)
+    return e4m3_encode(np.asarray(x, np.float32) * inv)
+
+
+def kv_append_fp8(k_new, v_new, cu_seqlens_new, cache_pos, k_cache, v_cache, k_scale, v_scale):
+    """kv_append into FP8 caches: the row of KV head g is quantized with that
+    head's scale (fp8_quantize) and written to its slot; slots outside
+    [0, max_ctx) are not written.  k_new, v_new: [T, Hkv, D] bf16; caches
+    [B, Hkv, max_ctx, D] uint8 codes; scales [Hkv] float32.
+    Returns new (k_cache, v_cache) uint8 tensors."""
+    kc, vc = k_cache.clone(), v_cache.clone()
+    cu = [int(x) for x in cu_seqlens_new]
+    pos = [int(x) for x in cache_pos]
+    ks = np.asarray(k_scale, np.float32)[None, :, None]
+    vs = np.asarray(v_scale, np.float32)[None, :, None]
+    kq = torch.from_numpy(fp8_quantize(k_new.float().numpy(), ks))    # [T, Hkv, D]
+    vq = torch.from_numpy(fp8_quantize(v_new.float().numpy(), vs))
+    max_ctx = kc.shape[2]
+    for b in range(len(cu) - 1):
+        for t in range(cu[b + 1] - cu[b]):
+            slot = pos[b] + t
+            if 0 <= slot < max_ctx:
+                kc[b, :, slot, :] = kq[cu[b] + t]
+                vc[b, :, slot, :] = vq[cu[b] + t]
+    return kc, vc
+
+
+def dequantize_fp8(codes, scales) -> np.ndarray:
+    """[B, Hkv, L, D] uint8 codes, [Hkv] scales -> float64 values."""
+    c = np.asarray(codes.numpy() if isinstance(codes, torch.Tensor) else codes, np.uint8)
+    s = np.asarray(scales, np.float32).astype(np.float64)
+    return E4M3_TABLE[c] * s[None, :, None, None]
+
+
+def decode_multi_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, sinks, *, scale=None,
+                     rows=None):
+    """Multi-token decode over FP8 caches (q_len >= 1 new tokens per request,
+    at the end of the cache; new token t sees tokens 0 .. len_b - q_len + t),
+    evaluated on the dequantized cache in float64, two passes per row:
+        x_j = scale * q . k_j,  M = max(s_h, max x),  Z = exp(s_h - M) + sum exp(x_j - M),
+        o = sum exp(x_j - M) v_j / Z,  lse = M + ln Z.
+    q: [B, q_len, Hq, D] bf16; codes [B, Hkv, max_ctx, D] uint8; scales [Hkv].
+    rows: (b, t, h) triples, default all in (b, t, h) order.
+    Returns (o [n, D], lse [n], sink_share [n]) float64.
+    """
+    qf = q.float().numpy().astype(np.float64)
+    B, q_len, Hq, D = qf.shape
+    Hkv = k_codes.shape[1]
+    r = Hq // Hkv
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    sk = sinks.to(torch.float32).numpy().astype(np.float64)
+    lens = [int(x) for x in seq_lens]
+    if rows is None:
+        rows = [(b, t, h) for b in range(B) for t in range(q_len) for h in range(Hq)]
+    kc = np.asarray(k_codes.numpy(), np.uint8)
+    vc = np.asarray(v_codes.numpy(), np.uint8)
+    ks = np.asarray(k_scale, np.float32).astype(np.float64)
+    vs = np.asarray(v_scale, np.float32).astype(np.float64)
+    o = np.zeros((len(rows), D), np.float64)
+    lse = np.zeros(len(rows), np.float64)
+    share = np.zeros(len(rows), np.float64)
+    by_bg = {}
+    for i, (b, t, h) in enumerate(rows):
+        by_bg.setdefault((b, h // r), []).append(i)
+    for (b, g), idx in by_bg.items():
+        n_max = max(0, lens[b])
+        K = E4M3_TABLE[kc[b, g, :n_max]] * ks[g]
+        V = E4M3_TABLE[vc[b, g, :n_max]] * vs[g]
+        for i in idx:
+            _, t, h = rows[i]
+            n = max(0, lens[b] - q_len + t + 1)
+            x = scale * (K[:n] @ qf[b, t, h])
+            s = sk[h]
+            M = max([s] + ([x.max()] if n else []))
+            if M == -math.inf:
+                lse[i] = -math.inf
+                continue
+            es = math.exp(s - M) if s != -math.inf else 0.0
+            e = np.exp(x - M)
+            Z = es + e.sum()
+            o[i] = (e @ V[:n]) / Z
+            lse[i] = M + math.log(Z)
+            share[i] = es / Z
+    return o, lse, share

@@ -519,3 +519,144 @@ def test_kv_append_then_decode_equals_prefill_last_row():
     o_d, lse_d, _ = oracle.decode(q[L - 1:L], kc, vc, torch.tensor([L], dtype=torch.int32), sinks)
     o_p, lse_p, _ = oracle.prefill(q, k, v, sinks, cu, rows=[(L - 1, h) for h in range(Hq)])
     assert np.array_equal(o_d, o_p) and np.array_equal(lse_d, lse_p)
+
+
+# ------------------------------------------------------------ FP8 KV cache --
+# Pins for the FP8 cache extension: the E4M3 table against torch's
+# float8_e4m3fn (a library routine) and against values fixed by the format;
+# the encoder's rounding, ties and saturation; the quantizer against torch's
+# conversion of the float32 product; the FP8 decode against the (separately
+# pinned) bf16 oracle where the dequantized cache is exact in bf16.
+
+def test_e4m3_table_matches_torch_float8_e4m3fn():
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    ours = oracle.E4M3_TABLE
+    assert np.array_equal(np.isnan(t), np.isnan(ours))
+    fin = ~np.isnan(t)
+    assert np.array_equal(t[fin], ours[fin])
+    assert np.array_equal(np.signbit(t[fin]), np.signbit(ours[fin]))
+
+
+def test_e4m3_values_fixed_by_the_format():
+    v = oracle.e4m3_value
+    assert v(0x7E) == 448.0 and v(0xFE) == -448.0           # largest finite
+    assert v(0x08) == 2.0 ** -6                             # smallest normal
+    assert v(0x01) == 2.0 ** -9 and v(0x07) == 7 * 2.0 ** -9  # subnormals
+    assert v(0x38) == 1.0 and v(0x39) == 1.125 and v(0xC0) == -2.0
+    assert v(0x00) == 0.0 and math.copysign(1.0, v(0x80)) == -1.0
+    assert math.isnan(v(0x7F)) and math.isnan(v(0xFF))
+    assert not any(math.isinf(v(c)) for c in range(256))
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)])
+    back = oracle.e4m3_encode(oracle.E4M3_TABLE[codes].astype(np.float32))
+    assert np.array_equal(back, codes)
+
+
+def test_e4m3_encode_rounding_ties_and_saturation():
+    cases = {
+        1.0625: 0x38,              # halfway 1.0 | 1.125: even mantissa (1.0)
+        1.1875: 0x3A,              # halfway 1.125 | 1.25: even mantissa (1.25)
+        1.05: 0x38, 1.1: 0x39,     # nearest
+        2.0 ** -10: 0x00,          # halfway 0 | 2^-9: to +0
+        -(2.0 ** -10): 0x80,       # ... to -0
+        3 * 2.0 ** -10: 0x02,      # halfway 2^-9 | 2^-8: even (2^-8)
+        2.0 ** -12: 0x00,
+        440.0: 0x7E, 449.0: 0x7E, 464.0: 0x7E, 1e30: 0x7E, -1e30: 0xFE,   # saturate
+        float("inf"): 0x7E, float("-inf"): 0xFE,
+    }
+    got = oracle.e4m3_encode(np.array(list(cases), np.float32))
+    assert [int(c) for c in got] == list(cases.values())
+    assert int(oracle.e4m3_encode([float("nan")])[0]) == 0x7F
+
+
+def test_e4m3_encode_matches_torch_on_in_range_values():
+    rng = np.random.default_rng(70)
+    x = np.concatenate([rng.normal(0, 30, 20000), rng.normal(0, 0.01, 5000),
+                        rng.uniform(-448, 448, 5000)]).astype(np.float32)
+    ours = oracle.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_fp8_quantize_is_the_float32_product_with_the_reciprocal():
+    rng = np.random.default_rng(71)
+    x = (rng.normal(0, 1, 20000) * rng.choice([0.1, 1, 10], 20000)).astype(np.float32)
+    for s in (0.0123, 1.0 / 3.0, 0.5, 2.5e-3):
+        inv = np.float32(1.0) / np.float32(s)
+        prod = torch.from_numpy(x * inv).clamp(-448, 448)
+        ref = prod.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(oracle.fp8_quantize(x, s), ref)
+
+
+def test_kv_append_fp8_places_quantized_rows():
+    g = torch.Generator().manual_seed(72)
+    B, Hkv, D, max_ctx = 3, 2, 16, 12
+    counts, pos = [3, 0, 5], [0, 4, 9]
+    kn, vn, cu, cp, _, _ = _append_case(g, counts, pos, B, Hkv, D, max_ctx)
+    kc = torch.randint(0, 256, (B, Hkv, max_ctx, D), generator=g, dtype=torch.uint8)
+    vc = torch.randint(0, 256, (B, Hkv, max_ctx, D), generator=g, dtype=torch.uint8)
+    ks, vs = np.float32([0.01, 0.003]), np.float32([0.02, 0.5])
+    ko, vo = oracle.kv_append_fp8(kn, vn, cu, cp, kc, vc, ks, vs)
+    written = set()
+    for b in range(B):
+        for t in range(counts[b]):
+            j = pos[b] + t
+            if j >= max_ctx:
+                continue
+            written.add((b, j))
+            for h in range(Hkv):
+                row_k = kn[int(cu[b]) + t, h].float().numpy()
+                row_v = vn[int(cu[b]) + t, h].float().numpy()
+                ref_k = torch.from_numpy((row_k * (np.float32(1) / ks[h])).clip(-448, 448))
+                ref_v = torch.from_numpy((row_v * (np.float32(1) / vs[h])).clip(-448, 448))
+                assert torch.equal(ko[b, h, j], ref_k.to(torch.float8_e4m3fn).view(torch.uint8))
+                assert torch.equal(vo[b, h, j], ref_v.to(torch.float8_e4m3fn).view(torch.uint8))
+    for b in range(B):
+        for j in range(max_ctx):
+            if (b, j) not in written:
+                assert torch.equal(ko[b, :, j], kc[b, :, j]) and torch.equal(vo[b, :, j], vc[b, :, j])
+
+
+def _fp8_decode_case(g, lens, q_len, Hq, Hkv, D, max_ctx):
+    B = len(lens)
+    q = _bf16_randn(g, B, q_len, Hq, D)
+    finite = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+    kc = finite[torch.randint(0, 254, (B, Hkv, max_ctx, D), generator=g)]
+    vc = finite[torch.randint(0, 254, (B, Hkv, max_ctx, D), generator=g)]
+    return q, kc, vc, torch.tensor(lens, dtype=torch.int32)
+
+
+def test_decode_fp8_equals_bf16_oracle_for_power_of_two_scales():
+    """With power-of-two scales every dequantized value is exact in bf16, so
+    the FP8 decode must equal the bf16 oracle run on that cache."""
+    g = torch.Generator().manual_seed(73)
+    lens, q_len, Hq, Hkv, D, max_ctx = [0, 1, 5, 40, 70], 3, 8, 2, 16, 72
+    q, kc, vc, sl = _fp8_decode_case(g, lens, q_len, Hq, Hkv, D, max_ctx)
+    ks, vs = np.float32([2.0 ** -7, 2.0 ** -5]), np.float32([2.0 ** -6, 2.0 ** -8])
+    sinks = torch.tensor([0.5, float("-inf"), 2.0, -1.0, 20.0, 0.0, 1.0, -3.0])
+    kd, vd = oracle.dequantize_fp8(kc, ks), oracle.dequantize_fp8(vc, vs)
+    kb, vb = torch.from_numpy(kd).to(torch.bfloat16), torch.from_numpy(vd).to(torch.bfloat16)
+    assert np.array_equal(kb.double().numpy(), kd) and np.array_equal(vb.double().numpy(), vd)
+    o8, l8, s8 = oracle.decode_multi_fp8(q, kc, vc, ks, vs, sl, sinks)
+    ob, lb, sb = oracle.decode_multi(q, kb, vb, sl, sinks)
+    np.testing.assert_allclose(o8, ob, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l8, lb, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s8, sb, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_fp8_scales_act_as_factors():
+    """k_scale multiplies every logit (the same as scaling the softmax scale);
+    v_scale multiplies the output."""
+    g = torch.Generator().manual_seed(74)
+    lens, Hq, Hkv, D = [9, 33], 4, 2, 16
+    q, kc, vc, sl = _fp8_decode_case(g, lens, 1, Hq, Hkv, D, 40)
+    sinks = torch.tensor([0.3, -1.0, 4.0, float("-inf")])
+    ks, vs = np.float32([0.01, 0.02]), np.float32([0.1, 0.3])
+    o1, l1, _ = oracle.decode_multi_fp8(q, kc, vc, ks, vs, sl, sinks, scale=0.25)
+    o2, l2, _ = oracle.decode_multi_fp8(q, kc, vc, ks * 2, vs, sl, sinks, scale=0.125)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12)
+    o3, _, _ = oracle.decode_multi_fp8(q, kc, vc, ks, vs * 4, sl, sinks, scale=0.25)
+    np.testing.assert_allclose(o3, 4 * o1, rtol=1e-12, atol=1e-14)
