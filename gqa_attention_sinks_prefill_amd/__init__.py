@@ -22,7 +22,8 @@ import torch
 
 __all__ = ["sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_split", "sink_attn_decode_multi_split",
            "sink_attn_merge_states", "sink_attn_decode", "sink_attn_decode_multi",
-           "sink_attn_kv_append",
+           "sink_attn_kv_append", "sink_attn_decode_multi_split_fp8", "sink_attn_decode_fp8",
+           "sink_attn_kv_append_fp8",
            "SinkAttnError", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -30,7 +31,8 @@ _LIB_PATH = os.path.join(_PKG, "libsinkattn.so")
 _lib = None
 
 EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_split", "sink_attn_decode_multi_split",
-                    "sink_attn_merge_states", "sink_attn_kv_append", "sink_attn_last_error")
+                    "sink_attn_decode_multi_split_fp8", "sink_attn_merge_states", "sink_attn_kv_append",
+                    "sink_attn_kv_append_fp8", "sink_attn_last_error")
 
 
 class SinkAttnError(RuntimeError):
@@ -75,6 +77,13 @@ def load_library():
     lib.sink_attn_kv_append.argtypes = [P, P, I64, I64, P, P, I32, I32, P, P, I64, I64, I64,
                                         I32, I32, I32, P]
     lib.sink_attn_kv_append.restype = ctypes.c_int
+    lib.sink_attn_decode_multi_split_fp8.argtypes = [P, I64, I64, I64, I32, P, P, I64, I64, I64,
+                                                     P, P, P, I32, I32, P, I32, I32, I32, F32,
+                                                     I32, I32, P, P, P, P]
+    lib.sink_attn_decode_multi_split_fp8.restype = ctypes.c_int
+    lib.sink_attn_kv_append_fp8.argtypes = [P, P, I64, I64, P, P, I32, I32, P, P, I64, I64, I64,
+                                            P, P, I32, I32, I32, P]
+    lib.sink_attn_kv_append_fp8.restype = ctypes.c_int
     lib.sink_attn_last_error.argtypes = []
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -362,4 +371,117 @@ def sink_attn_kv_append(k_new, v_new, cu_seqlens_new, cache_pos, k_cache, v_cach
         v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2), max_ctx,
         Hkv, D, _stream(stream))
     _check("sink_attn_kv_append", rc)
+    return k_cache, v_cache
+
+
+# ------------------------------------------------------------- FP8 caches --
+def _fp8_scales(k_scale, v_scale, Hkv):
+    for t, nm in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _dev(t, nm, torch.float32, 1)
+        if t.numel() != Hkv or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous fp32 tensor of num_kv_heads ({Hkv}) scales")
+
+
+def sink_attn_decode_multi_split_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, sinks,
+                                     split_size, num_splits=None, *, max_ctx=None, scale=None,
+                                     part_o=None, part_m=None, part_d=None, stream=None):
+    """sink_attn_decode_multi_split over FP8 E4M3 caches (uint8 codes
+    [B, Hkv, max_ctx, D]) with per-KV-head scales k_scale, v_scale [Hkv] fp32.
+    q: [B, q_len, Hq, D] bf16.  Returns the chunk states, as the bf16 form."""
+    _dev(q, "q", torch.bfloat16, 4)
+    _dev(k_cache, "k_cache", torch.uint8, 4)
+    _dev(v_cache, "v_cache", torch.uint8, 4)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    _dev(sinks, "sinks", torch.float32, 1)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if q.stride(3) != 1 or k_cache.stride(3) != 1:
+        raise ValueError("q and the caches need unit stride along head_dim")
+    B, q_len, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    _fp8_scales(k_scale, v_scale, Hkv)
+    max_ctx = k_cache.shape[2] if max_ctx is None else int(max_ctx)
+    if num_splits is None:
+        num_splits = -(-max_ctx // split_size)
+    shape = (B, q_len, Hq, num_splits)
+    if part_o is None:
+        part_o = torch.empty(*shape, D, dtype=torch.float32, device=q.device)
+        part_m = torch.empty(shape, dtype=torch.float32, device=q.device)
+        part_d = torch.empty(shape, dtype=torch.float32, device=q.device)
+    for t, nm, shp in ((part_o, "part_o", shape + (D,)), (part_m, "part_m", shape),
+                       (part_d, "part_d", shape)):
+        _dev(t, nm, torch.float32)
+        if not t.is_contiguous() or tuple(t.shape) != shp:
+            raise ValueError(f"{nm} must be contiguous with shape {shp}")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().sink_attn_decode_multi_split_fp8(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), q_len, k_cache.data_ptr(),
+        v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+        k_scale.data_ptr(), v_scale.data_ptr(), seq_lens.data_ptr(), B, max_ctx,
+        sinks.data_ptr(), Hq, Hkv, D, scale, int(split_size), int(num_splits),
+        part_o.data_ptr(), part_m.data_ptr(), part_d.data_ptr(), _stream(stream))
+    _check("sink_attn_decode_multi_split_fp8", rc)
+    return part_o, part_m, part_d
+
+
+def sink_attn_decode_fp8(q, k_cache, v_cache, k_scale, v_scale, seq_lens, sinks, split_size,
+                         num_splits=None, *, max_ctx=None, scale=None, out=None, lse=None,
+                         partials=None, stream=None):
+    """Decode over FP8 caches: q [B, Hq, D] (one new token) or [B, q_len, Hq, D];
+    sink_attn_decode_multi_split_fp8 then sink_attn_merge_states on one stream.
+    Returns out shaped like q (bf16)."""
+    q4 = q.unsqueeze(1) if q.dim() == 3 else q
+    B, q_len, Hq, D = q4.shape
+    po, pm, pd = partials if partials is not None else (None, None, None)
+    po, pm, pd = sink_attn_decode_multi_split_fp8(
+        q4, k_cache, v_cache, k_scale, v_scale, seq_lens, sinks, split_size, num_splits,
+        max_ctx=max_ctx, scale=scale, part_o=po, part_m=pm, part_d=pd, stream=stream)
+    S = po.shape[3]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    out4 = out.unsqueeze(1) if out.dim() == 3 else out
+    if tuple(out4.shape) != (B, q_len, Hq, D) or out4.stride(3) != 1:
+        raise ValueError("out must match q's shape with unit stride along head_dim")
+    if q_len == 1:
+        merged = out4[:, 0]
+    else:
+        if not out4.is_contiguous():
+            raise ValueError("out must be contiguous when q_len > 1")
+        merged = out4.view(B * q_len, Hq, D)
+    sink_attn_merge_states(po.view(B * q_len, Hq, S, D), pm.view(B * q_len, Hq, S),
+                           pd.view(B * q_len, Hq, S), out=merged, lse=lse, stream=stream)
+    return out
+
+
+def sink_attn_kv_append_fp8(k_new, v_new, cu_seqlens_new, cache_pos, k_cache, v_cache, k_scale,
+                            v_scale, *, max_new=None, stream=None):
+    """sink_attn_kv_append into FP8 E4M3 caches (uint8 [B, Hkv, max_ctx, D]):
+    each bf16 row of KV head g is quantized with 1 / k_scale[g] (v_scale[g])."""
+    _dev(k_new, "k_new", torch.bfloat16, 3)
+    _dev(v_new, "v_new", torch.bfloat16, 3)
+    _dev(cu_seqlens_new, "cu_seqlens_new", torch.int32, 1)
+    _dev(cache_pos, "cache_pos", torch.int32, 1)
+    _dev(k_cache, "k_cache", torch.uint8, 4)
+    _dev(v_cache, "v_cache", torch.uint8, 4)
+    if k_new.stride() != v_new.stride() or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must share shape and strides")
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if k_new.stride(2) != 1 or k_cache.stride(3) != 1:
+        raise ValueError("the new rows and the caches need unit stride along head_dim")
+    B, Hkv, max_ctx, D = k_cache.shape
+    _fp8_scales(k_scale, v_scale, Hkv)
+    S = cu_seqlens_new.numel() - 1
+    if cache_pos.numel() != S or k_new.shape[1] != Hkv or k_new.shape[2] != D:
+        raise ValueError("shapes of the new rows, cu_seqlens_new, cache_pos and caches disagree")
+    if S > B:
+        raise ValueError("more sequences than cache rows")
+    if max_new is None:
+        max_new = k_new.shape[0]
+    rc = load_library().sink_attn_kv_append_fp8(
+        k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_new.stride(1),
+        cu_seqlens_new.data_ptr(), cache_pos.data_ptr(), S, int(max_new), k_cache.data_ptr(),
+        v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+        k_scale.data_ptr(), v_scale.data_ptr(), max_ctx, Hkv, D, _stream(stream))
+    _check("sink_attn_kv_append_fp8", rc)
     return k_cache, v_cache

@@ -128,16 +128,18 @@ int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head
                                    scale, causal, o, o_stride_tok, o_stride_head, lse, stream);
 }
 
-int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
-                                 int64_t q_stride_head, int32_t q_len,
-                                 const void* k_cache, const void* v_cache, int64_t kv_stride_b,
-                                 int64_t kv_stride_head, int64_t kv_stride_tok,
-                                 const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
-                                 const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, float scale, int32_t split_size,
-                                 int32_t num_splits, float* part_o, float* part_m,
-                                 float* part_d, void* stream) {
-  g_err[0] = '\0';
+// Multi-token split decode over bf16 caches (k_scale == nullptr) or FP8 E4M3
+// caches with per-KV-head scales.
+static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                              int64_t q_stride_head, int32_t q_len, const void* k_cache,
+                              const void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
+                              int64_t kv_stride_tok, const float* k_scale, const float* v_scale,
+                              const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                              const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, float scale, int32_t split_size, int32_t num_splits,
+                              float* part_o, float* part_m, float* part_d, void* stream) {
+  const bool fp8 = k_scale != nullptr || v_scale != nullptr;
+  const int64_t elem = fp8 ? 1 : 2;           // bytes per cached element
   if (batch < 0 || max_ctx < 0) return fail(SINK_ATTN_EINVAL, "batch and max_ctx must be >= 0");
   if (q_len < 1) return fail(SINK_ATTN_EINVAL, "q_len must be >= 1 (got %d)", q_len);
   if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
@@ -151,16 +153,23 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
   if (batch == 0) return SINK_ATTN_OK;
   if (!q || !k_cache || !v_cache || !seq_lens || !sinks || !part_o || !part_m || !part_d)
     return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return fail(SINK_ATTN_EINVAL, "k_scale and v_scale must both be given, 4-byte aligned");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return fail(SINK_ATTN_EINVAL, "q, k_cache and v_cache must be 16-byte aligned");
   if (!aligned(seq_lens, 4) || !aligned(sinks, 4) || !aligned(part_o, 4) || !aligned(part_m, 4) ||
       !aligned(part_d, 4))
     return fail(SINK_ATTN_EINVAL, "seq_lens, sinks and the partial buffers must be 4-byte aligned");
-  if (!stride_ok(q_stride_b) || !stride_ok(q_stride_tok) || !stride_ok(q_stride_head) ||
-      !stride_ok(kv_stride_b) || !stride_ok(kv_stride_head) || !stride_ok(kv_stride_tok))
-    return fail(SINK_ATTN_EINVAL, "strides must be non-negative multiples of 8 elements");
+  if (!stride_ok(q_stride_b) || !stride_ok(q_stride_tok) || !stride_ok(q_stride_head))
+    return fail(SINK_ATTN_EINVAL, "query strides must be non-negative multiples of 8 elements");
+  // cache rows start on 16 bytes: 8 bf16 or 16 FP8 elements
+  const int64_t kv_mult = 16 / elem;
+  for (int64_t st : {kv_stride_b, kv_stride_head, kv_stride_tok})
+    if (st < 0 || st % kv_mult != 0)
+      return fail(SINK_ATTN_EINVAL, "cache strides must be non-negative multiples of %lld elements",
+                  static_cast<long long>(kv_mult));
   // a chunk of one head is addressed with 32-bit byte offsets
-  if (static_cast<int64_t>(split_size) * kv_stride_tok * 2 > 0x7fffffffLL)
+  if (static_cast<int64_t>(split_size) * kv_stride_tok * elem > 0x7fffffffLL)
     return fail(SINK_ATTN_EUNSUPPORTED, "split_size * kv_stride_tok spans more than 2 GiB");
 
   const int group = num_q_heads / num_kv_heads;
@@ -177,8 +186,10 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
   a.q_sb = q_stride_b;
   a.q_st = q_stride_tok;
   a.q_sh = q_stride_head;
-  a.k_cache = static_cast<const uint16_t*>(k_cache);
-  a.v_cache = static_cast<const uint16_t*>(v_cache);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = fp8 ? k_scale : nullptr;
+  a.v_scale = fp8 ? v_scale : nullptr;
   a.kv_sb = kv_stride_b;
   a.kv_sh = kv_stride_head;
   a.kv_st = kv_stride_tok;
@@ -199,6 +210,40 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
   a.scale_log2 = scale * 1.4426950408889634f;
   return launched(sinkattn::launch_decode_split(a, head_dim, num_blocks, static_cast<hipStream_t>(stream)),
                   "decode_split");
+}
+
+int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                                 int64_t q_stride_head, int32_t q_len,
+                                 const void* k_cache, const void* v_cache, int64_t kv_stride_b,
+                                 int64_t kv_stride_head, int64_t kv_stride_tok,
+                                 const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                                 const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float scale, int32_t split_size,
+                                 int32_t num_splits, float* part_o, float* part_m,
+                                 float* part_d, void* stream) {
+  g_err[0] = '\0';
+  return decode_multi_split(q, q_stride_b, q_stride_tok, q_stride_head, q_len, k_cache, v_cache,
+                            kv_stride_b, kv_stride_head, kv_stride_tok, nullptr, nullptr, seq_lens,
+                            batch, max_ctx, sinks, num_q_heads, num_kv_heads, head_dim, scale,
+                            split_size, num_splits, part_o, part_m, part_d, stream);
+}
+
+int sink_attn_decode_multi_split_fp8(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                                     int64_t q_stride_head, int32_t q_len, const void* k_cache,
+                                     const void* v_cache, int64_t kv_stride_b,
+                                     int64_t kv_stride_head, int64_t kv_stride_tok,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                                     const float* sinks, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, float scale,
+                                     int32_t split_size, int32_t num_splits, float* part_o,
+                                     float* part_m, float* part_d, void* stream) {
+  g_err[0] = '\0';
+  if (!k_scale || !v_scale) return fail(SINK_ATTN_EINVAL, "k_scale and v_scale are required");
+  return decode_multi_split(q, q_stride_b, q_stride_tok, q_stride_head, q_len, k_cache, v_cache,
+                            kv_stride_b, kv_stride_head, kv_stride_tok, k_scale, v_scale, seq_lens,
+                            batch, max_ctx, sinks, num_q_heads, num_kv_heads, head_dim, scale,
+                            split_size, num_splits, part_o, part_m, part_d, stream);
 }
 
 int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_head,
@@ -250,13 +295,13 @@ int sink_attn_merge_states(const float* part_o, const float* part_m, const float
   return launched(sinkattn::launch_merge(a, head_dim, static_cast<hipStream_t>(stream)), "merge_states");
 }
 
-int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride_tok,
-                        int64_t new_stride_head, const int32_t* cu_seqlens_new,
-                        const int32_t* cache_pos, int32_t num_seqs, int32_t max_new,
-                        void* k_cache, void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
-                        int64_t kv_stride_tok, int32_t max_ctx, int32_t num_kv_heads,
-                        int32_t head_dim, void* stream) {
-  g_err[0] = '\0';
+// KV append into bf16 caches (k_scale == nullptr: a copy) or FP8 E4M3 caches.
+static int kv_append(const void* k_new, const void* v_new, int64_t new_stride_tok,
+                     int64_t new_stride_head, const int32_t* cu_seqlens_new,
+                     const int32_t* cache_pos, int32_t num_seqs, int32_t max_new, void* k_cache,
+                     void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
+                     int64_t kv_stride_tok, const float* k_scale, const float* v_scale,
+                     int32_t max_ctx, int32_t num_kv_heads, int32_t head_dim, void* stream) {
   if (num_seqs < 0 || max_new < 0 || max_ctx < 0)
     return fail(SINK_ATTN_EINVAL, "num_seqs, max_new and max_ctx must be >= 0");
   if (num_kv_heads <= 0) return fail(SINK_ATTN_EINVAL, "num_kv_heads must be positive");
@@ -274,6 +319,8 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride
     return fail(SINK_ATTN_EINVAL, "strides must be non-negative multiples of 8 elements");
   if (k_new == k_cache || v_new == v_cache || k_cache == v_cache)
     return fail(SINK_ATTN_EINVAL, "the caches must not alias each other or the new rows");
+  if ((k_scale || v_scale) && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
+    return fail(SINK_ATTN_EINVAL, "k_scale and v_scale must both be given, 4-byte aligned");
 
   const int tpb = sinkattn::kv_append_tokens_per_block(head_dim);
   const int64_t token_blocks = (static_cast<int64_t>(max_new) + tpb - 1) / tpb;
@@ -287,8 +334,10 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride
   a.new_sh = new_stride_head;
   a.cu_seqlens_new = cu_seqlens_new;
   a.cache_pos = cache_pos;
-  a.k_cache = static_cast<uint16_t*>(k_cache);
-  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.kv_sb = kv_stride_b;
   a.kv_sh = kv_stride_head;
   a.kv_st = kv_stride_tok;
@@ -297,6 +346,33 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride
   a.token_blocks = static_cast<int32_t>(token_blocks);
   return launched(sinkattn::launch_kv_append(a, head_dim, num_blocks, static_cast<hipStream_t>(stream)),
                   "kv_append");
+}
+
+
+int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride_tok,
+                        int64_t new_stride_head, const int32_t* cu_seqlens_new,
+                        const int32_t* cache_pos, int32_t num_seqs, int32_t max_new,
+                        void* k_cache, void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
+                        int64_t kv_stride_tok, int32_t max_ctx, int32_t num_kv_heads,
+                        int32_t head_dim, void* stream) {
+  g_err[0] = '\0';
+  return kv_append(k_new, v_new, new_stride_tok, new_stride_head, cu_seqlens_new, cache_pos,
+                   num_seqs, max_new, k_cache, v_cache, kv_stride_b, kv_stride_head,
+                   kv_stride_tok, nullptr, nullptr, max_ctx, num_kv_heads, head_dim, stream);
+}
+
+int sink_attn_kv_append_fp8(const void* k_new, const void* v_new, int64_t new_stride_tok,
+                            int64_t new_stride_head, const int32_t* cu_seqlens_new,
+                            const int32_t* cache_pos, int32_t num_seqs, int32_t max_new,
+                            void* k_cache, void* v_cache, int64_t kv_stride_b,
+                            int64_t kv_stride_head, int64_t kv_stride_tok, const float* k_scale,
+                            const float* v_scale, int32_t max_ctx, int32_t num_kv_heads,
+                            int32_t head_dim, void* stream) {
+  g_err[0] = '\0';
+  if (!k_scale || !v_scale) return fail(SINK_ATTN_EINVAL, "k_scale and v_scale are required");
+  return kv_append(k_new, v_new, new_stride_tok, new_stride_head, cu_seqlens_new, cache_pos,
+                   num_seqs, max_new, k_cache, v_cache, kv_stride_b, kv_stride_head,
+                   kv_stride_tok, k_scale, v_scale, max_ctx, num_kv_heads, head_dim, stream);
 }
 
 }  // extern "C"

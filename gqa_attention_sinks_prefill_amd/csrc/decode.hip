@@ -56,6 +56,15 @@ constexpr int kSub = 64;                      // keys per sub-tile
 template <int DC> __device__ __forceinline__ int dv_swz(int row) {
   return 2 * ((row / (16 / DC)) & (DC / 2 - 1));
 }
+// The same for an FP8 (one byte per element) V sub-tile, read with the 8-bit
+// transposing read: the 32 lanes of a half-wave address 16 rows x two 8-byte
+// halves of one 16-byte chunk.  Rows hold 4 (D 64) or 8 (D 128) chunks, so
+// rows 4 (2) apart share bank slots; the XOR gives the rows that meet in a
+// half-wave different chunk slots (checked exhaustively on the host).
+template <int D> __device__ __forceinline__ int v8_swz(int row) {
+  if constexpr (D == 64) return ((row >> 2) + 2 * (row >> 4)) & 3;
+  return ((row >> 1) & 3) | ((row >> 2) & 4);
+}
 
 // fp32 values of the final merge of W waves' states: m and l of every column,
 // then o (none for a single wave, which writes its state directly).
@@ -63,28 +72,42 @@ template <int D, int CB, int W>
 constexpr int decode_merge_floats() {
   return W == 1 ? 0 : 2 * W * 16 * CB + W * D * 16 * CB;
 }
+// 16-bit LDS elements of one V sub-tile (bf16, or FP8 codes two to an element).
+template <int D, bool F8> constexpr int v_tile_elems() { return F8 ? kSub * D / 2 : kSub * D; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 // LDS of one decode workgroup (16-bit elements): two arrays of the waves' V
 // sub-tiles (even and odd sub-tiles), the first of them later reused for the
-// merge.  Two arrays rather than one with two halves: the compiler can then
-// see that a copy into one never aliases reads of the other, and does not make
-// the reads of sub-tile st wait for the copy of st + 1.
-template <int D, int CB, int W>
+// merge, and with one wave for the staged state (two column blocks of fp32 o
+// per array).  Two arrays rather than one with two halves: the compiler can
+// then see that a copy into one never aliases reads of the other, and does not
+// make the reads of sub-tile st wait for the copy of st + 1.
+template <int D, int CB, int W, bool F8>
 constexpr int decode_lds0_elems() {
-  return W * kSub * D > 2 * decode_merge_floats<D, CB, W>() ? W * kSub * D
-                                                             : 2 * decode_merge_floats<D, CB, W>();
+  return cmax(cmax(W * v_tile_elems<D, F8>(), 2 * decode_merge_floats<D, CB, W>()),
+              W == 1 ? 2 * (CB < 2 ? CB : 2) * 16 * D : 0);
+}
+template <int D, int CB, int W, bool F8>
+constexpr int decode_lds1_elems() {
+  return cmax(W * v_tile_elems<D, F8>(), W == 1 && CB > 2 ? 2 * (CB - 2) * 16 * D : 0);
 }
 
 // One work unit: chunk c of request b, KV head g, column slice hs, on W waves.
-template <int D, int CB, int W>
+// F8: the caches hold FP8 E4M3 codes with a dequantization scale per KV head;
+// the codes convert exactly to bf16 for the MFMAs, k_scale joins the softmax
+// scale and v_scale the final division by d.
+template <int D, int CB, int W, bool F8>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint16_t* v_lds0,
                                             uint16_t* v_lds1) {
-  constexpr int DC = D / 8;                  // 16-byte chunks per row
-  constexpr int TILE = kSub * D;             // elements of one V sub-tile
-  constexpr int NDMA = kSub * DC / 64;       // DMA instructions per V sub-tile
-  constexpr int NCC = D / 32;                // 32-d chunks of a K fragment row
+  constexpr int DC = D / 8;                  // 16-byte chunks per bf16 row
+  constexpr int RB = F8 ? D : 2 * D;         // bytes per cached row
+  constexpr int RC = RB / 16;                // 16-byte chunks per cached row
+  constexpr int TILE = v_tile_elems<D, F8>();
+  constexpr int NDMA = kSub * RB / 1024;     // DMA instructions per V sub-tile
+  constexpr int NCC = D / 32;                // 32-d contraction chunks of QK^T
+  constexpr int NKL = F8 ? D / 64 : NCC;     // 16-byte K loads per lane and 16-key block
   constexpr int NC = 16 * CB;                // columns of a workgroup
   constexpr int kMergeFloats = decode_merge_floats<D, CB, W>();
-  constexpr int kLds0Elems = decode_lds0_elems<D, CB, W>();
+  constexpr int kLds0Elems = decode_lds0_elems<D, CB, W, F8>();
   constexpr int kBlock = 64 * W;
 
   // units run chunk-major: the (often empty) late chunks of a ragged batch
@@ -146,10 +169,13 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
     const int tq = x / a.group;        // new token of the column
     const int h = g * a.group + x % a.group;
     n_lane[cb] = min(n, len - (a.q_len - 1 - tq) - lo);
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)tq * a.q_st + (int64_t)h * a.q_sh + 8 * lgrp;
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)tq * a.q_st + (int64_t)h * a.q_sh;
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
-      const u32x4_t t = load16(qp + 32 * cc);
+      // contraction chunk cc, lane row group lgrp: d = 32cc + 8lgrp .. +7; with
+      // FP8 K (16 codes per lane load): d = 64(cc/2) + 16lgrp + 8(cc%2) .. +7
+      const int d0 = F8 ? 64 * (cc >> 1) + 16 * lgrp + 8 * (cc & 1) : 32 * cc + 8 * lgrp;
+      const u32x4_t t = load16(qp + d0);
       qf[cb][cc] = valid ? t : u32x4_t{0, 0, 0, 0};
     }
     const float sink = valid ? a.sinks[h] : -INFINITY;
@@ -159,50 +185,79 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
     for (int db = 0; db < D / 16; ++db) acc[cb][db] = f32x4_t{};
   }
 
-  // K / V of this chunk through buffer resources (loads past its end read 0)
-  const int st2 = (int)(a.kv_st * 2);
-  const int64_t base = (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh + (int64_t)lo * a.kv_st;
-  const int nbytes = n > 0 ? (n - 1) * st2 + 2 * D : 0;
-  const auto krs = make_rsrc(a.k_cache + base, nbytes);
-  const auto vrs = make_rsrc(a.v_cache + base, nbytes);
+  // softmax scale (log2 units) of the raw dot products, and the factor of o
+  const float qk_scale = F8 ? a.scale_log2 * a.k_scale[g] : a.scale_log2;
+  const float out_scale = F8 ? a.v_scale[g] : 1.f;
 
-  // K fragment kb (16 keys) x cc (32 d): lane holds key kb*16 + col, d = 32cc + 8*lgrp
-  int k_off[NCC];
+  // K / V of this chunk through buffer resources (loads past its end read 0)
+  constexpr int EB = F8 ? 1 : 2;             // bytes per cached element
+  const int stb = (int)(a.kv_st * EB);       // bytes per cached token
+  const int64_t base = ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh + (int64_t)lo * a.kv_st) * EB;
+  const int nbytes = n > 0 ? (n - 1) * stb + RB : 0;
+  const auto krs = make_rsrc(static_cast<const char*>(a.k_cache) + base, nbytes);
+  const auto vrs = make_rsrc(static_cast<const char*>(a.v_cache) + base, nbytes);
+
+  // K fragment kb (16 keys): lane holds key kb*16 + col; bf16: load cc is
+  // d = 32cc + 8lgrp .. +7; FP8: load i is d = 64i + 16lgrp .. +15
+  int k_off[NKL];
 #pragma unroll
-  for (int cc = 0; cc < NCC; ++cc) k_off[cc] = col * st2 + (32 * cc + 8 * lgrp) * 2;
+  for (int i = 0; i < NKL; ++i) k_off[i] = col * stb + (F8 ? 64 * i + 16 * lgrp : (32 * i + 8 * lgrp) * 2);
   // V DMA: lane fills slot 64*i + lane = (row, physical chunk) of the sub-tile
   int v_goff[NDMA];
 #pragma unroll
   for (int i = 0; i < NDMA; ++i) {
-    const int s = 64 * i + lane, row = s / DC;
-    v_goff[i] = row * st2 + ((s % DC) ^ dv_swz<DC>(row)) * 16;
+    const int s = 64 * i + lane, row = s / RC;
+    v_goff[i] = row * stb + ((s % RC) ^ (F8 ? v8_swz<D>(row) : dv_swz<DC>(row))) * 16;
   }
-  // V^T transposing reads: row 32j + 16t + 4*lgrp + (col >> 2), d = 16*db + 4*(col & 3)
+  // V^T transposing reads (byte offsets in the sub-tile).  bf16: row
+  // 32j + 16t + 4*lgrp + (col >> 2), d = 16*db + 4*(col & 3).  FP8: lanes
+  // 2e, 2e+1 of row group lgrp address key 4lgrp + e (e < 4) or
+  // 16 + 4lgrp + e - 4 and the two 8-byte halves of d 16db .. +15, so that
+  // lane i receives d = 16db + i of those eight keys -- the keys and order of
+  // the P^T operand built from the S^T accumulators.
   int v_roff[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
-    const int row = 4 * lgrp + (col >> 2);
-    const int cl = 2 * db + ((col & 3) >> 1);
-    v_roff[db] = row * D + ((cl ^ dv_swz<DC>(row)) * 8) + 4 * (col & 1);
+    if constexpr (F8) {
+      const int e = col >> 1;
+      const int row = e < 4 ? 4 * lgrp + e : 16 + 4 * lgrp + e - 4;
+      v_roff[db] = row * RB + 16 * (db ^ v8_swz<D>(row)) + 8 * (col & 1);
+    } else {
+      const int row = 4 * lgrp + (col >> 2);
+      const int cl = 2 * db + ((col & 3) >> 1);
+      v_roff[db] = row * RB + ((cl ^ dv_swz<DC>(row)) * 16) + 8 * (col & 1);
+    }
   }
 
-  auto load_k = [&](int st, u32x4_t (&kf)[4][NCC]) {
-    const int off = st * kSub * st2;
+  auto load_k = [&](int st, u32x4_t (&kf)[4][NKL]) {
+    const int off = st * kSub * stb;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int cc = 0; cc < NCC; ++cc) kf[kb][cc] = buffer_load16<kNonTemporal>(krs, k_off[cc] + kb * 16 * st2 + off);
+      for (int i = 0; i < NKL; ++i) kf[kb][i] = buffer_load16<kNonTemporal>(krs, k_off[i] + kb * 16 * stb + off);
   };
   // Buffer numbers are compile-time constants (std::integral_constant).
   auto dma_v = [&](int st, auto buf) {
-    const int off = st * kSub * st2;
+    const int off = st * kSub * stb;
     uint16_t* dst = (decltype(buf)::value ? v_lds1 : v_lds0) + wave * TILE;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) buffer_load16_lds<kNonTemporal>(vrs, dst + i * 512, v_goff[i] + off);
   };
   // One 64-key sub-tile: every K operand and every V^T operand feeds the CB
   // column blocks' MFMAs.
-  auto compute = [&](int st, auto buf, const u32x4_t (&kf)[4][NCC]) {
+  auto compute = [&](int st, auto buf, const u32x4_t (&kf)[4][NKL]) {
+    u32x4_t kop[4][NCC];             // K operands (FP8 codes converted to bf16)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        if constexpr (F8) {
+          const u32x4_t raw = kf[kb][cc >> 1];
+          kop[kb][cc] = fp8x8_to_bf16x8(raw[2 * (cc & 1)], raw[2 * (cc & 1) + 1]);
+        } else {
+          kop[kb][cc] = kf[kb][cc];
+        }
+      }
     f32x4_t s[CB][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -210,7 +265,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
       for (int cb = 0; cb < CB; ++cb) {
         s[cb][kb] = f32x4_t{};
 #pragma unroll
-        for (int cc = 0; cc < NCC; ++cc) s[cb][kb] = mfma_16x16x32(kf[kb][cc], qf[cb][cc], s[cb][kb]);
+        for (int cc = 0; cc < NCC; ++cc) s[cb][kb] = mfma_16x16x32(kop[kb][cc], qf[cb][cc], s[cb][kb]);
       }
     const int k0 = st * kSub;
     if (k0 + kSub > n_all) {
@@ -235,7 +290,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
       mx = max3f(mx, sc[3][1], sc[3][2]);
       mx = fmaxf(mx, sc[3][3]);
       mx = pair32_max(pair16_max(mx));
-      const float m_new = fmaxf(m[cb], mx * a.scale_log2);
+      const float m_new = fmaxf(m[cb], mx * qk_scale);
       const float alpha = fast_exp2(m[cb] - m_new);
       m[cb] = m_new;
       float rs = 0.f;
@@ -243,7 +298,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(sc[kb][i], a.scale_log2, -m_new));
+          const float p = fast_exp2(__builtin_fmaf(sc[kb][i], qk_scale, -m_new));
           sc[kb][i] = p;
           rs += p;
         }
@@ -260,15 +315,21 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
         pf[cb][j][3] = pack_bf16x2(sc[2 * j + 1][2], sc[2 * j + 1][3]);
       }
     }
-    const uint16_t* vt = (decltype(buf)::value ? v_lds1 : v_lds0) + wave * TILE;
+    const char* vt = reinterpret_cast<const char*>((decltype(buf)::value ? v_lds1 : v_lds0) + wave * TILE);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        const uint16_t* vp = vt + v_roff[db] + 32 * j * D;
-        const u32x2_t v0 = lds_read_tr16(vp);
-        const u32x2_t v1 = lds_read_tr16(vp + 16 * D);
-        const u32x4_t vf = {v0[0], v0[1], v1[0], v1[1]};
+        const char* vp = vt + v_roff[db] + 32 * j * RB;
+        u32x4_t vf;
+        if constexpr (F8) {
+          const u32x2_t v = lds_read_tr8(vp);
+          vf = fp8x8_to_bf16x8(v[0], v[1]);
+        } else {
+          const u32x2_t v0 = lds_read_tr16(vp);
+          const u32x2_t v1 = lds_read_tr16(vp + 16 * RB);
+          vf = u32x4_t{v0[0], v0[1], v1[0], v1[1]};
+        }
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) acc[cb][db] = mfma_16x16x32(vf, pf[cb][j], acc[cb][db]);
       }
@@ -281,13 +342,13 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
   // passes per loop trip so the K register sets swap roles without copies.
   const std::integral_constant<int, 0> even{};
   const std::integral_constant<int, 1> odd{};
-  u32x4_t ka[4][NCC], kb2[4][NCC];
+  u32x4_t ka[4][NKL], kb2[4][NKL];
   int st = wave;
   if (st < n_sub) {
     load_k(st, ka);
     dma_v(st, even);
   }
-  auto pass = [&](auto buf, const u32x4_t (&kcur)[4][NCC], u32x4_t (&knext)[4][NCC]) {
+  auto pass = [&](auto buf, const u32x4_t (&kcur)[4][NKL], u32x4_t (&knext)[4][NKL]) {
     wait_vmem();
     if (st + W < n_sub) {
       load_k(st + W, knext);
@@ -310,12 +371,12 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
     // o / d of every column goes through LDS ([column][d] fp32, 16-byte
     // chunks XOR-swizzled by the column; the V buffers are free now) so that
     // part_o is written in whole rows.  Each V array holds two column blocks.
-    static_assert(2 * 16 * D * 2 <= kSub * D, "two column blocks of o fit one V array");
+    static_assert(2 * (CB < 2 ? CB : 2) * 16 * D <= kLds0Elems, "staged o fits the first array");
     __syncthreads();
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const float lt = pair32_sum(pair16_sum(l[cb]));
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float inv = lt > 0.f ? out_scale / lt : 0.f;
       float* stg = reinterpret_cast<float*>(cb < 2 ? v_lds0 : v_lds1) + (cb & 1) * 16 * D;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
@@ -375,7 +436,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
         o += *reinterpret_cast<const f32x4_t*>(red_o + (w * NC + xl) * D + 4 * (c4 ^ (xl & 15))) * f;
       }
       const int64_t row = out_row(x0 + xl);
-      const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+      const float inv = wsum > 0.f ? out_scale / wsum : 0.f;
       float* op = a.part_o + row * D + 4 * c4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) op[i] = o[i] * inv;
@@ -390,11 +451,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
 // One workgroup per unit.  head_dim 64 with up to 2 column blocks runs 2 waves
 // per SIMD (16 KB of LDS per wave); wider blocks and head_dim 128 need the
 // registers of 1 wave per SIMD.
-template <int D, int CB, int W>
+template <int D, int CB, int W, bool F8>
 __global__ __launch_bounds__(64 * W, (D == 64 && CB <= 2) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[decode_lds0_elems<D, CB, W>()];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[W * kSub * D];
-  decode_unit<D, CB, W>(a, blockIdx.x, v_lds0, v_lds1);
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[decode_lds0_elems<D, CB, W, F8>()];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[decode_lds1_elems<D, CB, W, F8>()];
+  decode_unit<D, CB, W, F8>(a, blockIdx.x, v_lds0, v_lds1);
 }
 
 // Wave-wide reductions (64 lanes) for the merge.
@@ -501,34 +562,37 @@ int decode_waves_per_unit(int64_t num_units, int head_dim, int column_blocks) {
   return num_units >= simds ? 1 : (2 * num_units >= simds ? 2 : 4);
 }
 
-template <int D, int CB>
+template <int D, int CB, bool F8>
 hipError_t launch_decode_cb(const DecodeArgs& a, int64_t num_units, int waves, hipStream_t stream) {
   const dim3 grid((unsigned)num_units);
   switch (waves) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<D, CB, 1>), grid, dim3(64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, CB, 2>), grid, dim3(128), 0, stream, a); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<D, CB, 4>), grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, CB, 1, F8>), grid, dim3(64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, CB, 2, F8>), grid, dim3(128), 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, CB, 4, F8>), grid, dim3(256), 0, stream, a); break;
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool F8>
 hipError_t launch_decode_d(const DecodeArgs& a, int64_t num_units, hipStream_t stream) {
   const int cb = decode_column_blocks(a.ncols, D);
   const int waves = decode_waves_per_unit(num_units, D, cb);
   switch (cb) {
-    case 1: return launch_decode_cb<D, 1>(a, num_units, waves, stream);
-    case 2: return launch_decode_cb<D, 2>(a, num_units, waves, stream);
+    case 1: return launch_decode_cb<D, 1, F8>(a, num_units, waves, stream);
+    case 2: return launch_decode_cb<D, 2, F8>(a, num_units, waves, stream);
     default:
-      if constexpr (D == 64) return launch_decode_cb<D, 4>(a, num_units, waves, stream);
+      if constexpr (D == 64) return launch_decode_cb<D, 4, F8>(a, num_units, waves, stream);
       return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,
                                hipStream_t stream) {
-  return head_dim == 64 ? launch_decode_d<64>(a, num_blocks, stream)
-                        : launch_decode_d<128>(a, num_blocks, stream);
+  if (a.k_scale != nullptr)
+    return head_dim == 64 ? launch_decode_d<64, true>(a, num_blocks, stream)
+                          : launch_decode_d<128, true>(a, num_blocks, stream);
+  return head_dim == 64 ? launch_decode_d<64, false>(a, num_blocks, stream)
+                        : launch_decode_d<128, false>(a, num_blocks, stream);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {

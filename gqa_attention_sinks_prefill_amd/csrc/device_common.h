@@ -122,6 +122,28 @@ __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
                                          __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
 }
+// Transposing 8-bit LDS read (ds_read_b64_tr_b8).  Within each group of 16
+// lanes, lane i receives byte (i & 7) of the 8-byte pieces addressed by lanes
+// 2k + (i >> 3), k = 0..7, as its bytes k = 0..7 (established by an in-bounds
+// probe of the instruction).
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2_t lds_read_tr8(const void* p) {
+  i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2_t*)(p));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+// Two OCP E4M3 codes (bytes 0-1 of `w`, or 2-3 when HI) -> two bf16, exactly
+// (every E4M3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// Eight codes (two words) -> the eight bf16 of one MFMA operand.
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4_t{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                 fp8x2_to_bf16x2<true>(w1)};
+}
+
 // max of three floats in one instruction (v_max3_f32)
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 

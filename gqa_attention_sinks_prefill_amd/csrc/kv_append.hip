@@ -9,7 +9,9 @@
 // tokens into their requests' caches: new token t of request b, KV head g,
 // goes to cache slot (b, g, cache_pos[b] + t).
 //
-// It is a pure copy (bytes in = bytes out, bit-exact), bound by HBM: one
+// It is a pure copy (bytes in = bytes out, bit-exact) into bf16 caches, or a
+// quantization into FP8 E4M3 caches with a scale per KV head (the code of x is
+// fp32(x) * (1 / scale) rounded to nearest even, saturated at +-448).  Bound by HBM: one
 // workgroup per (request, KV head, block of new tokens); each thread moves one
 // 16-byte chunk of K and of V per pass, the chunk index fastest so that the
 // stores of consecutive tokens of one head form one contiguous run.  Tokens
@@ -24,10 +26,33 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPasses = 4;                    // token rows per thread
+constexpr float kE4M3Max = 448.f;             // largest finite E4M3 value
 
-template <int D>
+// Eight values -> eight E4M3 codes of a cache with dequantization scale
+// 1 / inv: fp32(x) * inv, saturated to +-448, rounded to nearest even.
+__device__ __forceinline__ u32x2_t quantize8(const u32x4_t& bf, float inv) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(bf[i] << 16) * inv;
+    f[2 * i + 1] = __uint_as_float(bf[i] & 0xffff0000u) * inv;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)     // a NaN stays NaN (a NaN code)
+    f[i] = __builtin_isnan(f[i]) ? f[i] : fminf(fmaxf(f[i], -kE4M3Max), kE4M3Max);
+  u32x2_t r;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w], f[4 * w + 1], 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w + 2], f[4 * w + 3], v, true);
+    r[w] = (uint32_t)v;
+  }
+  return r;
+}
+
+template <int D, bool F8>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
-  constexpr int DC = D / 8;                   // 16-byte chunks per token row
+  constexpr int DC = D / 8;                   // 16-byte chunks per bf16 token row
   constexpr int TPP = kThreads / DC;          // tokens per pass
   constexpr int TB = TPP * kPasses;           // tokens per workgroup
   int unit = blockIdx.x;
@@ -55,12 +80,22 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
       vr[p] = load16(a.v_new + src);
     }
   }
+  float k_inv = 0.f, v_inv = 0.f;
+  if constexpr (F8) {
+    k_inv = 1.0f / a.k_scale[g];              // correctly rounded division
+    v_inv = 1.0f / a.v_scale[g];
+  }
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     if (ok[p]) {
       const int64_t dst = cache_row + (pos + t0 + p * TPP) * a.kv_st + 8 * c;
-      *reinterpret_cast<u32x4_t*>(a.k_cache + dst) = kr[p];
-      *reinterpret_cast<u32x4_t*>(a.v_cache + dst) = vr[p];
+      if constexpr (F8) {
+        *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.k_cache) + dst) = quantize8(kr[p], k_inv);
+        *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.v_cache) + dst) = quantize8(vr[p], v_inv);
+      } else {
+        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.k_cache) + dst) = kr[p];
+        *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.v_cache) + dst) = vr[p];
+      }
     }
   }
 }
@@ -72,10 +107,14 @@ int kv_append_tokens_per_block(int head_dim) { return kThreads / (head_dim / 8) 
 hipError_t launch_kv_append(const KvAppendArgs& a, int head_dim, int64_t num_blocks,
                             hipStream_t stream) {
   const dim3 grid((unsigned)num_blocks), block(kThreads);
-  if (head_dim == 64)
-    hipLaunchKernelGGL(kv_append_kernel<64>, grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL(kv_append_kernel<128>, grid, block, 0, stream, a);
+  const bool f8 = a.k_scale != nullptr;
+  if (head_dim == 64) {
+    if (f8) hipLaunchKernelGGL((kv_append_kernel<64, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((kv_append_kernel<64, false>), grid, block, 0, stream, a);
+  } else {
+    if (f8) hipLaunchKernelGGL((kv_append_kernel<128, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((kv_append_kernel<128, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -31,9 +31,11 @@ struct PrefillArgs {
 struct DecodeArgs {
   const uint16_t* q;
   int64_t q_sb, q_st, q_sh;  // request, new-token and head strides
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
-  int64_t kv_sb, kv_sh, kv_st;
+  const void* k_cache;       // bf16, or FP8 E4M3 codes when k_scale is set
+  const void* v_cache;
+  int64_t kv_sb, kv_sh, kv_st;  // in elements
+  const float* k_scale;      // FP8 caches: dequantization scale per KV head (else null)
+  const float* v_scale;
   const int32_t* seq_lens;
   const float* sinks;
   float* part_o;
@@ -69,9 +71,11 @@ struct KvAppendArgs {
   int64_t new_st, new_sh;  // token and head strides of the new rows
   const int32_t* cu_seqlens_new;
   const int32_t* cache_pos;
-  uint16_t* k_cache;
-  uint16_t* v_cache;
-  int64_t kv_sb, kv_sh, kv_st;
+  void* k_cache;            // bf16, or FP8 E4M3 codes when k_scale is set
+  void* v_cache;
+  int64_t kv_sb, kv_sh, kv_st;  // in elements
+  const float* k_scale;     // FP8 caches: dequantization scale per KV head (else null)
+  const float* v_scale;
   int32_t max_ctx;
   int32_t num_kv_heads;
   int32_t token_blocks;    // ceil(max_new / tokens per workgroup)

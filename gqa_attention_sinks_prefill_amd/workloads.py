@@ -246,3 +246,48 @@ def chunked_prefill_flops(seqlens_q, seqlens_k, num_q_heads: int, head_dim: int)
 def decode_kv_bytes(seq_lens, num_kv_heads: int, head_dim: int) -> float:
     """Algorithmic bytes: K and V of every cached token read once per KV head (bf16)."""
     return float(sum(int(n) for n in seq_lens)) * num_kv_heads * head_dim * 2 * 2
+
+
+# FP8 KV cache: the split-decode shape (64 requests x 8192 tokens, 64 q / 8 KV
+# heads, d 64) over E4M3 caches.  Codes are drawn uniformly from the 254
+# finite E4M3 codes (no quantizer runs here); per-KV-head scales U[0.005, 0.015]
+# put the dequantized values in about [-6.7, 6.7].
+FP8_DECODE = DecodeConfig("fp8_decode_b64_ctx8192_h64kv8_d64_split1024", 64, 8192, None, 8192,
+                          64, 8, 64, (-4.0, 4.0), split_size=1024, seed=8)
+FP8_SCALE_RANGE = (0.005, 0.015)
+
+
+def fp8_decode_inputs(cfg: DecodeConfig, lens=None) -> dict:
+    """CPU tensors for decode over FP8 caches: q (as decode_inputs), uint8 code
+    caches ``[B, Hkv, max_ctx, D]``, ``k_scale`` / ``v_scale`` ``[Hkv]`` fp32.
+    Draw order: lengths, Q, K codes, V codes, sinks, K scales, V scales; slots
+    at or beyond a request's length hold the NaN code 0x7F."""
+    g = torch.Generator("cpu").manual_seed(cfg.seed)
+    B, Hq, Hkv, D = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    if lens is not None:
+        lens = torch.tensor(list(lens), dtype=torch.int32)
+    elif cfg.ctx is not None:
+        lens = torch.full((B,), cfg.ctx, dtype=torch.int32)
+    else:
+        lo, hi = cfg.ctx_range
+        lens = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    qshape = (B, Hq, D) if cfg.q_len == 1 else (B, cfg.q_len, Hq, D)
+    q = torch.randn(qshape, generator=g).to(torch.bfloat16)
+    finite = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+    shape = (B, Hkv, cfg.max_ctx, D)
+    kc = finite[torch.randint(0, finite.numel(), shape, generator=g)]
+    vc = finite[torch.randint(0, finite.numel(), shape, generator=g)]
+    slot = torch.arange(cfg.max_ctx).view(1, 1, -1, 1)
+    unused = slot >= lens.view(-1, 1, 1, 1).to(torch.int64)
+    kc = kc.masked_fill(unused, 0x7F)
+    vc = vc.masked_fill(unused, 0x7F)
+    sinks = _sinks(g, Hq, cfg.sink_range, cfg.edge_sinks)
+    ks = torch.empty(Hkv, dtype=torch.float32).uniform_(*FP8_SCALE_RANGE, generator=g)
+    vs = torch.empty(Hkv, dtype=torch.float32).uniform_(*FP8_SCALE_RANGE, generator=g)
+    return dict(q=q, k_cache=kc, v_cache=vc, k_scale=ks, v_scale=vs, seq_lens=lens, sinks=sinks)
+
+
+def decode_kv_bytes_fp8(seq_lens, num_kv_heads: int, head_dim: int) -> float:
+    """Algorithmic bytes of decode over FP8 caches: K and V codes of every
+    cached token read once per KV head, one byte each."""
+    return float(sum(int(n) for n in seq_lens)) * num_kv_heads * head_dim * 2

@@ -233,6 +233,52 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride
                         int64_t kv_stride_tok, int32_t max_ctx, int32_t num_kv_heads,
                         int32_t head_dim, void* stream);
 
+/*
+ * FP8 KV cache.  The pages speak of FP8 only for weights; decode, though, is
+ * bound by the bytes of the cache it streams ("Hosting Qwen on Blackwell",
+ * section "Decoders"), and one byte per element halves them.  Format: OCP FP8
+ * E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; largest finite value 448), one byte per
+ * element, in the same HND layout as the bf16 caches, with one fp32
+ * dequantization scale per KV head: the cached value of KV head g is
+ * e4m3(code) * k_scale[g] (v_scale[g] for V).
+ *
+ * sink_attn_decode_multi_split_fp8: sink_attn_decode_multi_split over FP8
+ * caches -- the same chunk states (part_o, part_m, part_d, same shapes and
+ * meaning), computed on the dequantized cache.  Strides are in elements
+ * (= bytes) and must be multiples of 16; k_scale, v_scale [num_kv_heads]
+ * fp32, device, both required.  q_len = 1 is plain split decode.  Feed the
+ * partials to sink_attn_merge_states.  Errors: as
+ * sink_attn_decode_multi_split.
+ */
+int sink_attn_decode_multi_split_fp8(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                                     int64_t q_stride_head, int32_t q_len, const void* k_cache,
+                                     const void* v_cache, int64_t kv_stride_b,
+                                     int64_t kv_stride_head, int64_t kv_stride_tok,
+                                     const float* k_scale, const float* v_scale,
+                                     const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                                     const float* sinks, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, float scale,
+                                     int32_t split_size, int32_t num_splits, float* part_o,
+                                     float* part_m, float* part_d, void* stream);
+
+/*
+ * sink_attn_kv_append_fp8: sink_attn_kv_append into FP8 caches.  The new rows
+ * are bf16 as for sink_attn_kv_append; element x of KV head g is stored as the
+ * E4M3 code of fp32(x) * fp32(1 / k_scale[g]) (v_scale[g] for V): the
+ * reciprocal correctly rounded to fp32, the product rounded to fp32, then
+ * rounded to nearest (ties to even) and saturated to +-448; a NaN gives a NaN
+ * code.  Cache strides in elements (= bytes), multiples of 8.  Errors: as
+ * sink_attn_kv_append, plus SINK_ATTN_EINVAL for a missing scale.
+ */
+int sink_attn_kv_append_fp8(const void* k_new, const void* v_new, int64_t new_stride_tok,
+                            int64_t new_stride_head, const int32_t* cu_seqlens_new,
+                            const int32_t* cache_pos, int32_t num_seqs, int32_t max_new,
+                            void* k_cache, void* v_cache, int64_t kv_stride_b,
+                            int64_t kv_stride_head, int64_t kv_stride_tok, const float* k_scale,
+                            const float* v_scale, int32_t max_ctx, int32_t num_kv_heads,
+                            int32_t head_dim, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */
 const char* sink_attn_last_error(void);

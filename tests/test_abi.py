@@ -212,6 +212,83 @@ def test_kv_append_empty_work_is_a_noop():
     assert _kv_append(max_new=0)[0] == 0
 
 
+def _decode_multi_fp8(**kw):
+    a = dict(q=16, q_sb=4 * 4096, q_st=4096, q_sh=64, q_len=4, k=16, v=16,
+             kv_sb=8 * 1024 * 64, kv_sh=1024 * 64, kv_st=64, ks=4, vs=8, lens=4, batch=4,
+             max_ctx=1024, sinks=4, hq=64, hkv=8, d=64, scale=0.125, split=256, nsplit=4, po=4,
+             pm=4, pd=4)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_decode_multi_split_fp8(
+        a["q"], a["q_sb"], a["q_st"], a["q_sh"], a["q_len"], a["k"], a["v"], a["kv_sb"],
+        a["kv_sh"], a["kv_st"], a["ks"], a["vs"], a["lens"], a["batch"], a["max_ctx"],
+        a["sinks"], a["hq"], a["hkv"], a["d"], a["scale"], a["split"], a["nsplit"], a["po"],
+        a["pm"], a["pd"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ks=None), -1, "k_scale"),
+    (dict(vs=None), -1, "k_scale"),
+    (dict(ks=6), -1, "aligned"),
+    (dict(kv_st=72), -1, "multiples of 16"),
+    (dict(kv_sh=1024 * 64 + 8), -1, "multiples of 16"),
+    (dict(kv_st=1 << 22, split=1024), -2, "2 GiB"),
+    (dict(q_len=0), -1, "q_len"),
+    (dict(q_st=100), -1, "multiples of 8"),
+    (dict(q=None), -1, "null"),
+    (dict(split=96), -1, "split_size"),
+    (dict(nsplit=2), -1, "cover"),
+    (dict(d=32), -2, "head_dim"),
+    (dict(k=40), -1, "aligned"),
+])
+def test_decode_multi_split_fp8_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _decode_multi_fp8(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_decode_multi_split_fp8_empty_batch_is_a_noop():
+    assert _decode_multi_fp8(batch=0, q=None)[0] == 0
+
+
+def test_decode_split_size_times_stride_must_fit_32_bits():
+    rc, msg = _decode_multi(kv_st=1 << 21, split=1024)
+    assert rc == -2 and "2 GiB" in msg
+
+
+def _kv_append_fp8(**kw):
+    a = dict(kn=16, vn=32, n_st=512, n_sh=64, cu=4, pos=8, num_seqs=2, max_new=100, kc=48,
+             vc=64, kv_sb=8 * 1024 * 64, kv_sh=1024 * 64, kv_st=64, ks=4, vs=8, max_ctx=1024,
+             hkv=8, d=64)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_kv_append_fp8(a["kn"], a["vn"], a["n_st"], a["n_sh"], a["cu"], a["pos"],
+                                     a["num_seqs"], a["max_new"], a["kc"], a["vc"], a["kv_sb"],
+                                     a["kv_sh"], a["kv_st"], a["ks"], a["vs"], a["max_ctx"],
+                                     a["hkv"], a["d"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ks=None), -1, "k_scale"),
+    (dict(vs=None), -1, "k_scale"),
+    (dict(vs=6), -1, "aligned"),
+    (dict(kn=None), -1, "null"),
+    (dict(kc=40), -1, "aligned"),
+    (dict(d=96), -2, "head_dim"),
+    (dict(vc=48), -1, "alias"),
+])
+def test_kv_append_fp8_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _kv_append_fp8(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_kv_append_fp8_empty_work_is_a_noop():
+    assert _kv_append_fp8(num_seqs=0, kn=None)[0] == 0
+
+
 def _merge(**kw):
     a = dict(po=4, pm=4, pd=4, batch=2, hq=8, ns=4, d=64, o=16, o_sb=512, o_sh=64, lse=None)
     a.update(kw)

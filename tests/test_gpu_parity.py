@@ -540,3 +540,167 @@ def test_kv_append_from_a_fused_qkv_row():
     assert torch.equal(bkd.cpu()[::2].view(torch.int16), k_ref.view(torch.int16))
     assert torch.equal(bvd.cpu()[::2].view(torch.int16), v_ref.view(torch.int16))
     assert torch.equal(bkd.cpu()[1::2].view(torch.int16), big_k[1::2].view(torch.int16))
+
+
+# ------------------------------------------------------------ FP8 KV caches --
+def _fp8_cfg(lens, q_len, Hq, Hkv, D, seed, split, max_ctx=None, edges=None):
+    cfg = wl.DecodeConfig("fp8", len(lens), None, (1, 1), max_ctx or max(max(lens), 1), Hq, Hkv,
+                          D, (-4.0, 4.0), split_size=split, seed=seed, edge_sinks=edges or {},
+                          q_len=q_len)
+    return wl.fp8_decode_inputs(cfg, lens=lens)
+
+
+def _q4(q):
+    return q.unsqueeze(1) if q.dim() == 3 else q
+
+
+def _fp8_gpu(inp, split, ns=None):
+    q = _q4(inp["q"]).to(DEV)
+    kc, vc = inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    B, q_len, Hq, D = q.shape
+    ns = -(-kc.shape[2] // split) if ns is None else ns
+    po = torch.full((B, q_len, Hq, ns, D), float("nan"), device=DEV)
+    pm = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    pd = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    out = torch.full((B, q_len, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, q_len, Hq), float("nan"), device=DEV)
+    sa.sink_attn_decode_fp8(q, kc, vc, inp["k_scale"].to(DEV), inp["v_scale"].to(DEV),
+                            inp["seq_lens"].to(DEV), inp["sinks"].to(DEV), split, ns, out=out,
+                            lse=lse, partials=(po, pm, pd))
+    torch.cuda.synchronize()
+    return out, lse, (po, pm, pd)
+
+
+def _fp8_ref(inp, rows=None):
+    return oracle.decode_multi_fp8(_q4(inp["q"]), inp["k_cache"], inp["v_cache"],
+                                   inp["k_scale"].numpy(), inp["v_scale"].numpy(),
+                                   inp["seq_lens"], inp["sinks"], rows=rows)
+
+
+@pytest.mark.parametrize("q_len,Hq,Hkv,D", [(1, 64, 8, 64), (1, 64, 4, 128), (3, 64, 8, 64),
+                                             (2, 64, 4, 128), (8, 64, 8, 64), (1, 8, 8, 64)])
+def test_decode_fp8_all_rows(q_len, Hq, Hkv, D):
+    """FP8 caches against the oracle on every row: lengths 0, around 64-key
+    sub-tiles and chunk edges; unused slots hold the NaN code."""
+    lens = [0, q_len, 5, 64, 65, 257, 1000]
+    inp = _fp8_cfg(lens, q_len, Hq, Hkv, D, seed=100 + q_len + D, split=256,
+                   edges={0: float("-inf"), Hq - 1: 20.0})
+    out, lse, _ = _fp8_gpu(inp, 256)
+    o_ref, lse_ref, _ = _fp8_ref(inp)
+    assert_close(out.reshape(-1, D), o_ref, what=f"fp8 decode q_len={q_len} Hq={Hq} D={D}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="fp8 decode lse")
+
+
+def test_decode_fp8_over_a_quantized_normal_cache():
+    """Caches made by quantizing normal bf16 K/V with the oracle's quantizer."""
+    g = torch.Generator().manual_seed(101)
+    lens, Hq, Hkv, D, max_ctx = [1, 200, 300], 32, 4, 64, 320
+    B = len(lens)
+    k = torch.randn(B, Hkv, max_ctx, D, generator=g)
+    v = torch.randn(B, Hkv, max_ctx, D, generator=g)
+    ks = np.float32([0.004 * (1 + h) for h in range(Hkv)])
+    vs = np.float32([0.02 / (1 + h) for h in range(Hkv)])
+    kc = torch.from_numpy(oracle.fp8_quantize(k.numpy(), ks[None, :, None, None]))
+    vc = torch.from_numpy(oracle.fp8_quantize(v.numpy(), vs[None, :, None, None]))
+    inp = dict(q=torch.randn(B, Hq, D, generator=g).to(torch.bfloat16), k_cache=kc, v_cache=vc,
+               k_scale=torch.from_numpy(ks), v_scale=torch.from_numpy(vs),
+               seq_lens=torch.tensor(lens, dtype=torch.int32),
+               sinks=torch.empty(Hq).uniform_(-4, 4, generator=g))
+    out, lse, _ = _fp8_gpu(inp, 128)
+    o_ref, lse_ref, _ = _fp8_ref(inp)
+    assert_close(out.reshape(-1, D), o_ref, what="fp8 decode, quantized normal cache")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="fp8 decode lse, quantized normal cache")
+
+
+@pytest.mark.parametrize("B,Hkv,D,q_len,split", [
+    (128, 8, 64, 1, 64),      # one column block: four waves per chunk
+    (128, 8, 64, 3, 64),      # two blocks, 8192 chunks: a wave per chunk
+    (24, 8, 64, 3, 128),      # two blocks, 768 chunks: two waves per chunk
+    (32, 8, 64, 8, 128),      # four blocks: a wave per chunk
+    (64, 8, 128, 1, 128),     # head_dim 128: a wave per chunk
+])
+def test_decode_fp8_work_splits_edge_lengths(B, Hkv, D, q_len, split):
+    """Each way waves share a chunk, FP8 caches, edge lengths (zero included),
+    every chunk state checked (empty chunks exactly (0, -inf, 0))."""
+    lens = [_EDGE_LENS[(5 * i) % len(_EDGE_LENS)] for i in range(B)]
+    inp = _fp8_cfg(lens, q_len, 64, Hkv, D, seed=110 + q_len + D + split, split=split,
+                   max_ctx=512, edges={0: float("-inf"), 63: 20.0})
+    ns = 512 // split
+    out, lse, (po, pm, pd) = _fp8_gpu(inp, split, ns)
+    o_ref, lse_ref, _ = _fp8_ref(inp)
+    what = f"fp8 decode B={B} D={D} q_len={q_len} split={split}"
+    assert_close(out.reshape(-1, D), o_ref, what=what)
+    assert_lse_close(lse.reshape(-1), lse_ref, what=f"{what} lse")
+    po, pm, pd = po.cpu(), pm.cpu(), pd.cpu()
+    assert not torch.isnan(po).any() and not torch.isnan(pm).any() and not torch.isnan(pd).any()
+    for b, L in enumerate(lens):
+        first_empty = max(-(-L // split), 1)
+        assert torch.all(po[b, :, :, first_empty:] == 0)
+        assert torch.all(pm[b, :, :, first_empty:] == float("-inf"))
+        assert torch.all(pd[b, :, :, first_empty:] == 0)
+
+
+def test_decode_fp8_full_config_sampled_rows():
+    """64 requests x 8192 tokens over FP8 caches (the bench's FP8 decode line)."""
+    cfg = wl.FP8_DECODE
+    inp = wl.fp8_decode_inputs(cfg)
+    out, lse, _ = _fp8_gpu(inp, cfg.split_size)
+    assert not torch.isnan(out).any().item()
+    g = torch.Generator().manual_seed(8)
+    rows = sorted({(int(torch.randint(cfg.batch, (1,), generator=g)), 0,
+                    int(torch.randint(cfg.num_q_heads, (1,), generator=g))) for _ in range(96)}
+                  | {(0, 0, 0), (cfg.batch - 1, 0, cfg.num_q_heads - 1)})
+    o_ref, lse_ref, _ = _fp8_ref(inp, rows=rows)
+    idx = torch.tensor(rows)
+    assert_close(out.cpu()[idx[:, 0], 0, idx[:, 2]], o_ref, what="fp8 decode full config")
+    assert_lse_close(lse.cpu()[idx[:, 0], 0, idx[:, 2]], lse_ref, what="fp8 decode full config lse")
+
+
+@pytest.mark.parametrize("Hkv,D", [(8, 64), (4, 128), (1, 64)])
+def test_kv_append_fp8_bitwise(Hkv, D):
+    """Quantizing append against the oracle, code for code; slots outside the
+    cache are dropped and untouched slots keep their codes."""
+    counts, max_ctx = [3, 0, 130, 64, 200], 256
+    d = wl.kv_append_inputs(counts, max_ctx, Hkv, D, seed=120 + D, pos=[0, 5, 100, 192, 250])
+    g = torch.Generator().manual_seed(121)
+    B = len(counts)
+    kc = torch.randint(0, 256, (B, Hkv, max_ctx, D), generator=g, dtype=torch.uint8)
+    vc = torch.randint(0, 256, (B, Hkv, max_ctx, D), generator=g, dtype=torch.uint8)
+    ks = torch.empty(Hkv).uniform_(0.002, 0.02, generator=g)
+    vs = torch.empty(Hkv).uniform_(0.002, 0.02, generator=g)
+    kn = (d["k_new"].float() * 3).to(torch.bfloat16)      # some values saturate at +-448
+    vn = d["v_new"]
+    ko, vo = oracle.kv_append_fp8(kn, vn, d["cu_seqlens_new"], d["cache_pos"], kc, vc,
+                                  ks.numpy(), vs.numpy())
+    kg, vg = kc.to(DEV), vc.to(DEV)
+    sa.sink_attn_kv_append_fp8(kn.to(DEV), vn.to(DEV), d["cu_seqlens_new"].to(DEV),
+                               d["cache_pos"].to(DEV), kg, vg, ks.to(DEV), vs.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(kg.cpu(), ko) and torch.equal(vg.cpu(), vo)
+
+
+def test_kv_append_fp8_then_decode():
+    """Append bf16 rows into empty FP8 caches on the GPU, then decode over them:
+    equal to the oracle decode over the oracle's own quantized caches."""
+    g = torch.Generator().manual_seed(122)
+    counts, Hq, Hkv, D, max_ctx = [37, 300, 129], 64, 8, 64, 320
+    d = wl.kv_append_inputs(counts, max_ctx, Hkv, D, seed=123, pos=[0, 0, 0])
+    ks = torch.empty(Hkv).uniform_(0.005, 0.02, generator=g)
+    vs = torch.empty(Hkv).uniform_(0.005, 0.02, generator=g)
+    B = len(counts)
+    zero = torch.zeros(B, Hkv, max_ctx, D, dtype=torch.uint8)
+    ko, vo = oracle.kv_append_fp8(d["k_new"], d["v_new"], d["cu_seqlens_new"], d["cache_pos"],
+                                  zero, zero, ks.numpy(), vs.numpy())
+    kg, vg = zero.to(DEV), zero.clone().to(DEV)
+    sa.sink_attn_kv_append_fp8(d["k_new"].to(DEV), d["v_new"].to(DEV),
+                               d["cu_seqlens_new"].to(DEV), d["cache_pos"].to(DEV), kg, vg,
+                               ks.to(DEV), vs.to(DEV))
+    inp = dict(q=torch.randn(B, Hq, D, generator=g).to(torch.bfloat16), k_cache=kg.cpu(),
+               v_cache=vg.cpu(), k_scale=ks, v_scale=vs,
+               seq_lens=torch.tensor(counts, dtype=torch.int32),
+               sinks=torch.empty(Hq).uniform_(-4, 4, generator=g))
+    assert torch.equal(inp["k_cache"], ko) and torch.equal(inp["v_cache"], vo)
+    out, lse, _ = _fp8_gpu(inp, 64)
+    o_ref, lse_ref, _ = _fp8_ref(inp)
+    assert_close(out.reshape(-1, D), o_ref, what="fp8 append then decode")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="fp8 append then decode lse")
