@@ -23,9 +23,9 @@ of prefill rows on this host, scaled to TFLOP/s.
 After the timed steps (not part of them): `hbm_read_reference` times a plain
 streaming-read kernel (libhbmprobe.so) and `decode.frac_of_measured_read`
 relates the decode to it; `extra` holds the other workloads' lines -- the
-head_dim 128 varlen prefill, chunked prefill, multi-token decode, KV-cache
-append and the ragged long-context decode at B = 1, 8, 32, 128 (B < 32 is
-launch / latency bound and flagged so).
+head_dim 128 varlen prefill, chunked prefill, multi-token decode, decode over
+FP8 caches, KV-cache append and the ragged long-context decode at B = 1, 8,
+32, 128 (B < 32 is launch / latency bound and flagged so).
 """
 from __future__ import annotations
 
@@ -241,6 +241,43 @@ def multi_decode_measurement(dev, stream, reps: int):
             "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def fp8_decode_measurement(dev, stream, reps: int):
+    """Decode over FP8 (E4M3) caches: 64 requests x 8192 tokens, 64 / 8 heads,
+    d 64, split 1024 + merge, event-timed.  GB/s of the one-byte codes read
+    (half the bytes of the bf16 line for the same tokens)."""
+    cfg = wl.FP8_DECODE
+    inp = wl.fp8_decode_inputs(cfg)
+    q, kc, vc = inp["q"].to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    ks, vs = inp["k_scale"].to(dev), inp["v_scale"].to(dev)
+    lens, sinks = inp["seq_lens"].to(dev), inp["sinks"].to(dev)
+    B, Hq, D = q.shape
+    ns = cfg.num_splits
+    po = torch.empty(B, 1, Hq, ns, D, device=dev)
+    pm = torch.empty(B, 1, Hq, ns, device=dev)
+    pd = torch.empty(B, 1, Hq, ns, device=dev)
+    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    run = lambda: sa.sink_attn_decode_fp8(q, kc, vc, ks, vs, lens, sinks, cfg.split_size, ns,
+                                          scale=cfg.scale, out=out, partials=(po, pm, pd),
+                                          stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+         for _ in range(reps)]
+    for a, b in e:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
+    kv = wl.decode_kv_bytes_fp8(inp["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
+    gbs = kv / (ms * 1e-3) / 1e9
+    return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
+            "metric": "decode FP8 KV GB/s (split + merge)", "mean_ms": round(ms, 4),
+            "algorithmic_bytes_per_step": kv,
+            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def hbm_read_reference(dev, stream, reps: int = 10):
     """GB/s of a plain streaming-read kernel (libhbmprobe.so, built beside the
     library): 4 GiB read once per launch, each workgroup a contiguous slice,
@@ -439,7 +476,7 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(split_gbs / PEAK_HBM_GBS, 4),
-                                "traffic": traffic_d, "kernel": "decode_split_kernel<64,1,4>",
+                                "traffic": traffic_d, "kernel": "decode_split_kernel<64,1,4,false>",
                                 "algorithmic_bytes_per_launch": kv_bytes},
                    "frac_of_hbm_peak_incl_merge": round(dec_gbs / PEAK_HBM_GBS, 4)},
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
@@ -449,6 +486,7 @@ def main():
         res["extra"] = [varlen_prefill_measurement(dev, stream, max(3, args.steps // 2)),
                         chunked_prefill_measurement(dev, stream, max(3, args.steps // 2)),
                         multi_decode_measurement(dev, stream, max(3, args.steps // 2)),
+                        fp8_decode_measurement(dev, stream, max(3, args.steps // 2)),
                         kv_append_measurement(dev, stream, max(3, args.steps // 2))]
         res["extra"] += [ragged_decode_measurement(dev, stream, b, max(3, args.steps // 4))
                          for b in wl.RAGGED_BATCHES]
