@@ -459,3 +459,67 @@ def decode_multi_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, sinks, *, 
             lse[i] = M + math.log(Z)
             share[i] = es / Z
     return o, lse, share
+
+
+# --------------------------------------------------------- paged KV cache --
+# The pages keep caches in HND order per request; a paged (block-table) cache
+# is the serving-engine form of the same data and is a plain extension (not on
+# the pages).  Reading taken: physical pages [num_pages, Hkv, page_size, D]
+# (HND inside a page); request b's logical token j lives in page
+# block_tables[b, j // page_size], slot j % page_size.  Attention over it is the
+# definition above on the logical cache; the oracle gathers that cache with
+# plain indexing and evaluates the existing definitions.
+
+def gather_pages(pages, block_tables, page_size, length):
+    """Logical caches [B, Hkv, length, D] from pages [num_pages, Hkv, P, D] and
+    block_tables [B, >= ceil(length / P)] (int); a copy, dtype preserved."""
+    B = block_tables.shape[0]
+    num_pages, Hkv, P, D = pages.shape
+    if P != page_size:
+        raise ValueError("pages' third dimension must be page_size")
+    out = torch.empty((B, Hkv, length, D), dtype=pages.dtype)
+    for b in range(B):
+        for j in range(length):
+            out[b, :, j] = pages[int(block_tables[b, j // P]), :, j % P]
+    return out
+
+
+def decode_multi_paged(q, k_pages, v_pages, block_tables, page_size, seq_lens, sinks, *,
+                       k_scale=None, v_scale=None, scale=None, rows=None):
+    """Multi-token decode over a paged cache (bf16 pages, or FP8 E4M3 code pages
+    when k_scale / v_scale are given): gather each request's logical cache,
+    then decode_multi / decode_multi_fp8.  q: [B, q_len, Hq, D]."""
+    L = max([int(x) for x in seq_lens] + [1])
+    kc = gather_pages(k_pages, block_tables, page_size, L)
+    vc = gather_pages(v_pages, block_tables, page_size, L)
+    if k_scale is None:
+        return decode_multi(q, kc, vc, seq_lens, sinks, scale=scale, rows=rows)
+    return decode_multi_fp8(q, kc, vc, k_scale, v_scale, seq_lens, sinks, scale=scale, rows=rows)
+
+
+def kv_append_paged(k_new, v_new, cu_seqlens_new, cache_pos, k_pages, v_pages, block_tables,
+                    page_size, *, k_scale=None, v_scale=None):
+    """Append into a paged cache: new token t of request b goes to logical slot
+    cache_pos[b] + t, i.e. page block_tables[b, slot // P], slot % P; slots
+    at or past (table width) * P are dropped.  bf16 rows are copied, or
+    quantized (fp8_quantize, per KV head) when k_scale / v_scale are given.
+    Returns new (k_pages, v_pages)."""
+    kp, vp = k_pages.clone(), v_pages.clone()
+    cu = [int(x) for x in cu_seqlens_new]
+    pos = [int(x) for x in cache_pos]
+    width = block_tables.shape[1]
+    if k_scale is not None:
+        kq = torch.from_numpy(fp8_quantize(k_new.float().numpy(),
+                                           np.asarray(k_scale, np.float32)[None, :, None]))
+        vq = torch.from_numpy(fp8_quantize(v_new.float().numpy(),
+                                           np.asarray(v_scale, np.float32)[None, :, None]))
+    else:
+        kq, vq = k_new, v_new
+    for b in range(len(cu) - 1):
+        for t in range(cu[b + 1] - cu[b]):
+            slot = pos[b] + t
+            if 0 <= slot < width * page_size:
+                page = int(block_tables[b, slot // page_size])
+                kp[page, :, slot % page_size] = kq[cu[b] + t]
+                vp[page, :, slot % page_size] = vq[cu[b] + t]
+    return kp, vp

@@ -660,3 +660,110 @@ def test_decode_fp8_scales_act_as_factors():
     np.testing.assert_allclose(l1, l2, rtol=1e-12)
     o3, _, _ = oracle.decode_multi_fp8(q, kc, vc, ks, vs * 4, sl, sinks, scale=0.25)
     np.testing.assert_allclose(o3, 4 * o1, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------- paged KV cache --
+# Pins for the paged cache: pages scattered by a hand-written loop under a
+# random table and gathered back must give the logical cache bit for bit, and
+# every paged function must equal its (separately pinned) contiguous form.
+
+def _scatter_pages(logical, P, num_pages, g):
+    """Scatter logical caches [B, Hkv, L, D] into num_pages pages of P slots by
+    a random permutation; returns (pages, block_tables)."""
+    B, Hkv, L, D = logical.shape
+    per = -(-L // P)
+    perm = torch.randperm(num_pages, generator=g)[:B * per].view(B, per).to(torch.int32)
+    pages = torch.zeros((num_pages, Hkv, P, D), dtype=logical.dtype)
+    for b in range(B):
+        for j in range(L):
+            pages[int(perm[b, j // P]), :, j % P] = logical[b, :, j]
+    return pages, perm
+
+
+def test_gather_pages_inverts_a_random_scatter():
+    g = torch.Generator().manual_seed(80)
+    logical = _bf16_randn(g, 3, 2, 45, 8)
+    for P in (1, 4, 16, 64):
+        pages, bt = _scatter_pages(logical, P, 3 * (-(-45 // P)) + 5, g)
+        back = oracle.gather_pages(pages, bt, P, 45)
+        assert torch.equal(back.view(torch.int16), logical.view(torch.int16))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_paged_equals_contiguous(fp8):
+    g = torch.Generator().manual_seed(81 + fp8)
+    lens, q_len, Hq, Hkv, D, L = [0, 1, 15, 16, 17, 40], 2, 8, 2, 16, 48
+    B = len(lens)
+    q = _bf16_randn(g, B, q_len, Hq, D)
+    if fp8:
+        finite = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+        kl = finite[torch.randint(0, 254, (B, Hkv, L, D), generator=g)]
+        vl = finite[torch.randint(0, 254, (B, Hkv, L, D), generator=g)]
+        scales = dict(k_scale=np.float32([0.01, 0.02]), v_scale=np.float32([0.03, 0.005]))
+    else:
+        kl, vl = _bf16_randn(g, B, Hkv, L, D), _bf16_randn(g, B, Hkv, L, D)
+        scales = {}
+    sinks = torch.tensor([0.5, float("-inf"), 2.0, -1.0, 20.0, 0.0, 1.0, -3.0])
+    sl = torch.tensor(lens, dtype=torch.int32)
+    P = 16
+    kp, bt = _scatter_pages(kl, P, 40, g)
+    vp = torch.zeros_like(kp)
+    for b in range(B):
+        for j in range(L):
+            vp[int(bt[b, j // P]), :, j % P] = vl[b, :, j]
+    o_p, l_p, _ = oracle.decode_multi_paged(q, kp, vp, bt, P, sl, sinks, **scales)
+    if fp8:
+        o_c, l_c, _ = oracle.decode_multi_fp8(q, kl, vl, scales["k_scale"], scales["v_scale"], sl, sinks)
+    else:
+        o_c, l_c, _ = oracle.decode_multi(q, kl, vl, sl, sinks)
+    assert np.array_equal(o_p, o_c) and np.array_equal(l_p, l_c)
+
+
+def test_decode_paged_with_shared_prefix_pages():
+    """Two requests whose tables share their first page (a shared prefix) equal
+    contiguous caches holding copies of it."""
+    g = torch.Generator().manual_seed(83)
+    Hq, Hkv, D, P = 4, 1, 8, 4
+    pages = _bf16_randn(g, 6, Hkv, P, D)
+    bt = torch.tensor([[0, 1, 2], [0, 3, 4]], dtype=torch.int32)
+    sl = torch.tensor([10, 12], dtype=torch.int32)
+    logical = torch.stack([torch.cat([pages[int(p)] for p in bt[b]], dim=1) for b in range(2)])
+    q = _bf16_randn(g, 2, 1, Hq, D)
+    sinks = torch.tensor([0.0, 1.0, -1.0, float("-inf")])
+    o_p, _, _ = oracle.decode_multi_paged(q, pages, pages, bt, P, sl, sinks)
+    o_c, _, _ = oracle.decode_multi(q, logical, logical, sl, sinks)
+    assert np.array_equal(o_p, o_c)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_kv_append_paged_equals_contiguous_append(fp8):
+    """Append into pages then gather equals the contiguous append into the
+    logical cache; slots past the table's capacity are dropped."""
+    g = torch.Generator().manual_seed(84 + fp8)
+    B, Hkv, D, P, width = 3, 2, 16, 8, 3           # capacity 24 slots per request
+    counts, pos = [5, 0, 9], [3, 7, 20]            # request 2: slots 20..28, 24.. dropped
+    kn, vn, cu, cp, _, _ = _append_case(g, counts, pos, B, Hkv, D, width * P)
+    num_pages = 12
+    bt = torch.randperm(num_pages, generator=g)[:B * width].view(B, width).to(torch.int32)
+    if fp8:
+        kp = torch.randint(0, 256, (num_pages, Hkv, P, D), generator=g, dtype=torch.uint8)
+        vp = torch.randint(0, 256, (num_pages, Hkv, P, D), generator=g, dtype=torch.uint8)
+        ks, vs = np.float32([0.01, 0.03]), np.float32([0.02, 0.004])
+        kp2, vp2 = oracle.kv_append_paged(kn, vn, cu, cp, kp, vp, bt, P, k_scale=ks, v_scale=vs)
+    else:
+        kp, vp = _bf16_randn(g, num_pages, Hkv, P, D), _bf16_randn(g, num_pages, Hkv, P, D)
+        kp2, vp2 = oracle.kv_append_paged(kn, vn, cu, cp, kp, vp, bt, P)
+    kl = oracle.gather_pages(kp, bt, P, width * P)
+    vl = oracle.gather_pages(vp, bt, P, width * P)
+    if fp8:
+        kl2, vl2 = oracle.kv_append_fp8(kn, vn, cu, cp, kl, vl, ks, vs)
+    else:
+        kl2, vl2 = oracle.kv_append(kn, vn, cu, cp, kl, vl)
+    same = (lambda a, b: torch.equal(a, b)) if fp8 else \
+        (lambda a, b: torch.equal(a.view(torch.int16), b.view(torch.int16)))
+    assert same(oracle.gather_pages(kp2, bt, P, width * P), kl2)
+    assert same(oracle.gather_pages(vp2, bt, P, width * P), vl2)
+    used = set(int(x) for x in bt.flatten())
+    for p in range(num_pages):                     # pages outside every table: untouched
+        if p not in used:
+            assert same(kp2[p], kp[p]) and same(vp2[p], vp[p])
