@@ -23,7 +23,8 @@ import torch
 __all__ = ["sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_split", "sink_attn_decode_multi_split",
            "sink_attn_merge_states", "sink_attn_decode", "sink_attn_decode_multi",
            "sink_attn_kv_append", "sink_attn_decode_multi_split_fp8", "sink_attn_decode_fp8",
-           "sink_attn_kv_append_fp8",
+           "sink_attn_kv_append_fp8", "sink_attn_decode_paged_split", "sink_attn_decode_paged",
+           "sink_attn_kv_append_paged",
            "SinkAttnError", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,8 +32,9 @@ _LIB_PATH = os.path.join(_PKG, "libsinkattn.so")
 _lib = None
 
 EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_split", "sink_attn_decode_multi_split",
-                    "sink_attn_decode_multi_split_fp8", "sink_attn_merge_states", "sink_attn_kv_append",
-                    "sink_attn_kv_append_fp8", "sink_attn_last_error")
+                    "sink_attn_decode_multi_split_fp8", "sink_attn_decode_paged_split",
+                    "sink_attn_merge_states", "sink_attn_kv_append", "sink_attn_kv_append_fp8",
+                    "sink_attn_kv_append_paged", "sink_attn_last_error")
 
 
 class SinkAttnError(RuntimeError):
@@ -84,6 +86,13 @@ def load_library():
     lib.sink_attn_kv_append_fp8.argtypes = [P, P, I64, I64, P, P, I32, I32, P, P, I64, I64, I64,
                                             P, P, I32, I32, I32, P]
     lib.sink_attn_kv_append_fp8.restype = ctypes.c_int
+    lib.sink_attn_decode_paged_split.argtypes = [P, I64, I64, I64, I32, P, P, I64, I64, I64, I32,
+                                                 P, I64, I32, P, P, P, I32, P, I32, I32, I32, F32,
+                                                 I32, I32, P, P, P, P]
+    lib.sink_attn_decode_paged_split.restype = ctypes.c_int
+    lib.sink_attn_kv_append_paged.argtypes = [P, P, I64, I64, P, P, I32, I32, P, P, I64, I64, I64,
+                                              I32, P, I64, I32, P, P, I32, I32, P]
+    lib.sink_attn_kv_append_paged.restype = ctypes.c_int
     lib.sink_attn_last_error.argtypes = []
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -485,3 +494,124 @@ def sink_attn_kv_append_fp8(k_new, v_new, cu_seqlens_new, cache_pos, k_cache, v_
         k_scale.data_ptr(), v_scale.data_ptr(), max_ctx, Hkv, D, _stream(stream))
     _check("sink_attn_kv_append_fp8", rc)
     return k_cache, v_cache
+
+
+# ------------------------------------------------------------ paged caches --
+def _paged_common(k_pages, v_pages, block_tables, k_scale, v_scale):
+    dtype = torch.bfloat16 if k_scale is None else torch.uint8
+    if (k_scale is None) != (v_scale is None):
+        raise ValueError("give both k_scale and v_scale (FP8 pages) or neither (bf16 pages)")
+    _dev(k_pages, "k_pages", dtype, 4)
+    _dev(v_pages, "v_pages", dtype, 4)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    if k_pages.stride() != v_pages.stride() or k_pages.shape != v_pages.shape:
+        raise ValueError("k_pages and v_pages must share shape and strides")
+    if k_pages.stride(3) != 1 or block_tables.stride(1) != 1:
+        raise ValueError("pages need unit stride along head_dim, block_tables along its rows")
+    if k_scale is not None:
+        _fp8_scales(k_scale, v_scale, k_pages.shape[1])
+
+
+def sink_attn_decode_paged_split(q, k_pages, v_pages, block_tables, seq_lens, sinks, split_size,
+                                 num_splits=None, *, k_scale=None, v_scale=None, scale=None,
+                                 part_o=None, part_m=None, part_d=None, stream=None):
+    """Chunk states of (multi-token) decode over a paged cache: pages
+    [num_pages, Hkv, page_size, D] (bf16, or FP8 E4M3 codes with k_scale /
+    v_scale), block_tables [B, pages_per_seq] int32; q [B, q_len, Hq, D]."""
+    _dev(q, "q", torch.bfloat16, 4)
+    _paged_common(k_pages, v_pages, block_tables, k_scale, v_scale)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    _dev(sinks, "sinks", torch.float32, 1)
+    if q.stride(3) != 1:
+        raise ValueError("q needs unit stride along head_dim")
+    B, q_len, Hq, D = q.shape
+    _, Hkv, P, _ = k_pages.shape
+    pages_per_seq = block_tables.shape[1]
+    if block_tables.shape[0] < B:
+        raise ValueError("block_tables needs a row per request")
+    if num_splits is None:
+        num_splits = -(-(pages_per_seq * P) // split_size)
+    shape = (B, q_len, Hq, num_splits)
+    if part_o is None:
+        part_o = torch.empty(*shape, D, dtype=torch.float32, device=q.device)
+        part_m = torch.empty(shape, dtype=torch.float32, device=q.device)
+        part_d = torch.empty(shape, dtype=torch.float32, device=q.device)
+    for t, nm, shp in ((part_o, "part_o", shape + (D,)), (part_m, "part_m", shape),
+                       (part_d, "part_d", shape)):
+        _dev(t, nm, torch.float32)
+        if not t.is_contiguous() or tuple(t.shape) != shp:
+            raise ValueError(f"{nm} must be contiguous with shape {shp}")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().sink_attn_decode_paged_split(
+        q.data_ptr(), q.stride(0), q.stride(1), q.stride(2), q_len, k_pages.data_ptr(),
+        v_pages.data_ptr(), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), P,
+        block_tables.data_ptr(), block_tables.stride(0), pages_per_seq,
+        None if k_scale is None else k_scale.data_ptr(),
+        None if v_scale is None else v_scale.data_ptr(), seq_lens.data_ptr(), B,
+        sinks.data_ptr(), Hq, Hkv, D, scale, int(split_size), int(num_splits),
+        part_o.data_ptr(), part_m.data_ptr(), part_d.data_ptr(), _stream(stream))
+    _check("sink_attn_decode_paged_split", rc)
+    return part_o, part_m, part_d
+
+
+def sink_attn_decode_paged(q, k_pages, v_pages, block_tables, seq_lens, sinks, split_size,
+                           num_splits=None, *, k_scale=None, v_scale=None, scale=None, out=None,
+                           lse=None, partials=None, stream=None):
+    """Decode over a paged cache: sink_attn_decode_paged_split then
+    sink_attn_merge_states on one stream.  q [B, Hq, D] or [B, q_len, Hq, D];
+    returns out shaped like q (bf16)."""
+    q4 = q.unsqueeze(1) if q.dim() == 3 else q
+    B, q_len, Hq, D = q4.shape
+    po, pm, pd = partials if partials is not None else (None, None, None)
+    po, pm, pd = sink_attn_decode_paged_split(
+        q4, k_pages, v_pages, block_tables, seq_lens, sinks, split_size, num_splits,
+        k_scale=k_scale, v_scale=v_scale, scale=scale, part_o=po, part_m=pm, part_d=pd,
+        stream=stream)
+    S = po.shape[3]
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    out4 = out.unsqueeze(1) if out.dim() == 3 else out
+    if tuple(out4.shape) != (B, q_len, Hq, D) or out4.stride(3) != 1:
+        raise ValueError("out must match q's shape with unit stride along head_dim")
+    if q_len == 1:
+        merged = out4[:, 0]
+    else:
+        if not out4.is_contiguous():
+            raise ValueError("out must be contiguous when q_len > 1")
+        merged = out4.view(B * q_len, Hq, D)
+    sink_attn_merge_states(po.view(B * q_len, Hq, S, D), pm.view(B * q_len, Hq, S),
+                           pd.view(B * q_len, Hq, S), out=merged, lse=lse, stream=stream)
+    return out
+
+
+def sink_attn_kv_append_paged(k_new, v_new, cu_seqlens_new, cache_pos, k_pages, v_pages,
+                              block_tables, *, k_scale=None, v_scale=None, max_new=None,
+                              stream=None):
+    """Append new tokens' K/V rows [T, Hkv, D] into a paged cache through its
+    block table (a copy into bf16 pages, or quantizing into FP8 pages)."""
+    _dev(k_new, "k_new", torch.bfloat16, 3)
+    _dev(v_new, "v_new", torch.bfloat16, 3)
+    _dev(cu_seqlens_new, "cu_seqlens_new", torch.int32, 1)
+    _dev(cache_pos, "cache_pos", torch.int32, 1)
+    _paged_common(k_pages, v_pages, block_tables, k_scale, v_scale)
+    if k_new.stride() != v_new.stride() or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must share shape and strides")
+    if k_new.stride(2) != 1:
+        raise ValueError("the new rows need unit stride along head_dim")
+    _, Hkv, P, D = k_pages.shape
+    S = cu_seqlens_new.numel() - 1
+    if cache_pos.numel() != S or k_new.shape[1] != Hkv or k_new.shape[2] != D:
+        raise ValueError("shapes of the new rows, cu_seqlens_new, cache_pos and pages disagree")
+    if block_tables.shape[0] < S:
+        raise ValueError("block_tables needs a row per request")
+    if max_new is None:
+        max_new = k_new.shape[0]
+    rc = load_library().sink_attn_kv_append_paged(
+        k_new.data_ptr(), v_new.data_ptr(), k_new.stride(0), k_new.stride(1),
+        cu_seqlens_new.data_ptr(), cache_pos.data_ptr(), S, int(max_new), k_pages.data_ptr(),
+        v_pages.data_ptr(), k_pages.stride(0), k_pages.stride(1), k_pages.stride(2), P,
+        block_tables.data_ptr(), block_tables.stride(0), block_tables.shape[1],
+        None if k_scale is None else k_scale.data_ptr(),
+        None if v_scale is None else v_scale.data_ptr(), Hkv, D, _stream(stream))
+    _check("sink_attn_kv_append_paged", rc)
+    return k_pages, v_pages

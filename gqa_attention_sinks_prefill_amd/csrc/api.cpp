@@ -129,18 +129,28 @@ int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head
 }
 
 // Multi-token split decode over bf16 caches (k_scale == nullptr) or FP8 E4M3
-// caches with per-KV-head scales.
+// caches with per-KV-head scales; per-request caches, or pages through a block
+// table (block_tables != nullptr: kv_stride_b is then the page stride).
 static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
                               int64_t q_stride_head, int32_t q_len, const void* k_cache,
                               const void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
                               int64_t kv_stride_tok, const float* k_scale, const float* v_scale,
+                              const int32_t* block_tables, int64_t bt_stride, int32_t page_size,
                               const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
                               const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, float scale, int32_t split_size, int32_t num_splits,
                               float* part_o, float* part_m, float* part_d, void* stream) {
   const bool fp8 = k_scale != nullptr || v_scale != nullptr;
+  const bool paged = page_size != 0;
   const int64_t elem = fp8 ? 1 : 2;           // bytes per cached element
   if (batch < 0 || max_ctx < 0) return fail(SINK_ATTN_EINVAL, "batch and max_ctx must be >= 0");
+  int page_shift = 0;
+  if (paged) {
+    if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+      return fail(SINK_ATTN_EINVAL, "page_size must be a power of two in [16, 2^20] (got %d)", page_size);
+    while ((1 << page_shift) < page_size) ++page_shift;
+    if (bt_stride < 0) return fail(SINK_ATTN_EINVAL, "block_tables row stride must be >= 0");
+  }
   if (q_len < 1) return fail(SINK_ATTN_EINVAL, "q_len must be >= 1 (got %d)", q_len);
   if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
   if (int rc = check_scale(scale)) return rc;
@@ -150,9 +160,16 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
   if (static_cast<int64_t>(num_splits) * split_size < max_ctx)
     return fail(SINK_ATTN_EINVAL, "num_splits * split_size (%lld) does not cover max_ctx (%d)",
                 static_cast<long long>(num_splits) * split_size, max_ctx);
+  // a chunk spans at most split/page + 1 pages; the kernel holds 256 entries
+  if (paged && (split_size + page_size - 1) / page_size + 1 > 256)
+    return fail(SINK_ATTN_EUNSUPPORTED, "split_size %d spans more than 255 pages of %d tokens",
+                split_size, page_size);
   if (batch == 0) return SINK_ATTN_OK;
-  if (!q || !k_cache || !v_cache || !seq_lens || !sinks || !part_o || !part_m || !part_d)
+  if (!q || !k_cache || !v_cache || !seq_lens || !sinks || !part_o || !part_m || !part_d ||
+      (paged && !block_tables))
     return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  if (paged && !aligned(block_tables, 4))
+    return fail(SINK_ATTN_EINVAL, "block_tables must be 4-byte aligned");
   if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
     return fail(SINK_ATTN_EINVAL, "k_scale and v_scale must both be given, 4-byte aligned");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
@@ -168,8 +185,8 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
     if (st < 0 || st % kv_mult != 0)
       return fail(SINK_ATTN_EINVAL, "cache strides must be non-negative multiples of %lld elements",
                   static_cast<long long>(kv_mult));
-  // a chunk of one head is addressed with 32-bit byte offsets
-  if (static_cast<int64_t>(split_size) * kv_stride_tok * elem > 0x7fffffffLL)
+  // a chunk (a 16-key block of a page) of one head is addressed with 32-bit offsets
+  if (static_cast<int64_t>(paged ? 16 : split_size) * kv_stride_tok * elem > 0x7fffffffLL)
     return fail(SINK_ATTN_EUNSUPPORTED, "split_size * kv_stride_tok spans more than 2 GiB");
 
   const int group = num_q_heads / num_kv_heads;
@@ -190,9 +207,13 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
   a.v_cache = v_cache;
   a.k_scale = fp8 ? k_scale : nullptr;
   a.v_scale = fp8 ? v_scale : nullptr;
-  a.kv_sb = kv_stride_b;
+  a.kv_sb = paged ? 0 : kv_stride_b;
   a.kv_sh = kv_stride_head;
   a.kv_st = kv_stride_tok;
+  a.block_tables = paged ? block_tables : nullptr;
+  a.bt_stride = bt_stride;
+  a.kv_sp = paged ? kv_stride_b : 0;
+  a.page_shift = page_shift;
   a.seq_lens = seq_lens;
   a.sinks = sinks;
   a.part_o = part_o;
@@ -223,7 +244,8 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
                                  float* part_d, void* stream) {
   g_err[0] = '\0';
   return decode_multi_split(q, q_stride_b, q_stride_tok, q_stride_head, q_len, k_cache, v_cache,
-                            kv_stride_b, kv_stride_head, kv_stride_tok, nullptr, nullptr, seq_lens,
+                            kv_stride_b, kv_stride_head, kv_stride_tok, nullptr, nullptr, nullptr, 0,
+                            0, seq_lens,
                             batch, max_ctx, sinks, num_q_heads, num_kv_heads, head_dim, scale,
                             split_size, num_splits, part_o, part_m, part_d, stream);
 }
@@ -241,9 +263,35 @@ int sink_attn_decode_multi_split_fp8(const void* q, int64_t q_stride_b, int64_t 
   g_err[0] = '\0';
   if (!k_scale || !v_scale) return fail(SINK_ATTN_EINVAL, "k_scale and v_scale are required");
   return decode_multi_split(q, q_stride_b, q_stride_tok, q_stride_head, q_len, k_cache, v_cache,
-                            kv_stride_b, kv_stride_head, kv_stride_tok, k_scale, v_scale, seq_lens,
+                            kv_stride_b, kv_stride_head, kv_stride_tok, k_scale, v_scale, nullptr, 0,
+                            0, seq_lens,
                             batch, max_ctx, sinks, num_q_heads, num_kv_heads, head_dim, scale,
                             split_size, num_splits, part_o, part_m, part_d, stream);
+}
+
+int sink_attn_decode_paged_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                                 int64_t q_stride_head, int32_t q_len, const void* k_pages,
+                                 const void* v_pages, int64_t page_stride, int64_t kv_stride_head,
+                                 int64_t kv_stride_tok, int32_t page_size,
+                                 const int32_t* block_tables, int64_t bt_stride,
+                                 int32_t pages_per_seq, const float* k_scale, const float* v_scale,
+                                 const int32_t* seq_lens, int32_t batch, const float* sinks,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 float scale, int32_t split_size, int32_t num_splits,
+                                 float* part_o, float* part_m, float* part_d, void* stream) {
+  g_err[0] = '\0';
+  if ((k_scale == nullptr) != (v_scale == nullptr))
+    return fail(SINK_ATTN_EINVAL, "k_scale and v_scale must both be given or both be null");
+  if (page_size <= 0) return fail(SINK_ATTN_EINVAL, "page_size must be a power of two in [16, 2^20] (got %d)", page_size);
+  if (pages_per_seq < 0) return fail(SINK_ATTN_EINVAL, "pages_per_seq must be >= 0");
+  const int64_t max_ctx = static_cast<int64_t>(pages_per_seq) * page_size;
+  if (max_ctx > 0x7fffffff) return fail(SINK_ATTN_EUNSUPPORTED, "pages_per_seq * page_size exceeds 2^31");
+  return decode_multi_split(q, q_stride_b, q_stride_tok, q_stride_head, q_len, k_pages, v_pages,
+                            page_stride, kv_stride_head, kv_stride_tok, k_scale, v_scale,
+                            block_tables, bt_stride, page_size, seq_lens, batch,
+                            static_cast<int32_t>(max_ctx), sinks, num_q_heads, num_kv_heads,
+                            head_dim, scale, split_size, num_splits, part_o, part_m, part_d,
+                            stream);
 }
 
 int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_head,
@@ -301,15 +349,27 @@ static int kv_append(const void* k_new, const void* v_new, int64_t new_stride_to
                      const int32_t* cache_pos, int32_t num_seqs, int32_t max_new, void* k_cache,
                      void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
                      int64_t kv_stride_tok, const float* k_scale, const float* v_scale,
+                     const int32_t* block_tables, int64_t bt_stride, int32_t page_size,
                      int32_t max_ctx, int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  const bool paged = page_size != 0;
+  int page_shift = 0;
+  if (paged) {
+    if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1)) != 0)
+      return fail(SINK_ATTN_EINVAL, "page_size must be a power of two in [16, 2^20] (got %d)", page_size);
+    while ((1 << page_shift) < page_size) ++page_shift;
+    if (bt_stride < 0) return fail(SINK_ATTN_EINVAL, "block_tables row stride must be >= 0");
+  }
   if (num_seqs < 0 || max_new < 0 || max_ctx < 0)
     return fail(SINK_ATTN_EINVAL, "num_seqs, max_new and max_ctx must be >= 0");
   if (num_kv_heads <= 0) return fail(SINK_ATTN_EINVAL, "num_kv_heads must be positive");
   if (head_dim != 64 && head_dim != 128)
     return fail(SINK_ATTN_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", head_dim);
   if (num_seqs == 0 || max_new == 0 || max_ctx == 0) return SINK_ATTN_OK;
-  if (!k_new || !v_new || !cu_seqlens_new || !cache_pos || !k_cache || !v_cache)
+  if (!k_new || !v_new || !cu_seqlens_new || !cache_pos || !k_cache || !v_cache ||
+      (paged && !block_tables))
     return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  if (paged && !aligned(block_tables, 4))
+    return fail(SINK_ATTN_EINVAL, "block_tables must be 4-byte aligned");
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return fail(SINK_ATTN_EINVAL, "k_new, v_new and the caches must be 16-byte aligned");
   if (!aligned(cu_seqlens_new, 4) || !aligned(cache_pos, 4))
@@ -338,6 +398,9 @@ static int kv_append(const void* k_new, const void* v_new, int64_t new_stride_to
   a.v_cache = v_cache;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.block_tables = paged ? block_tables : nullptr;
+  a.bt_stride = bt_stride;
+  a.page_shift = page_shift;
   a.kv_sb = kv_stride_b;
   a.kv_sh = kv_stride_head;
   a.kv_st = kv_stride_tok;
@@ -358,7 +421,8 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride
   g_err[0] = '\0';
   return kv_append(k_new, v_new, new_stride_tok, new_stride_head, cu_seqlens_new, cache_pos,
                    num_seqs, max_new, k_cache, v_cache, kv_stride_b, kv_stride_head,
-                   kv_stride_tok, nullptr, nullptr, max_ctx, num_kv_heads, head_dim, stream);
+                   kv_stride_tok, nullptr, nullptr, nullptr, 0, 0, max_ctx, num_kv_heads, head_dim,
+                   stream);
 }
 
 int sink_attn_kv_append_fp8(const void* k_new, const void* v_new, int64_t new_stride_tok,
@@ -372,7 +436,29 @@ int sink_attn_kv_append_fp8(const void* k_new, const void* v_new, int64_t new_st
   if (!k_scale || !v_scale) return fail(SINK_ATTN_EINVAL, "k_scale and v_scale are required");
   return kv_append(k_new, v_new, new_stride_tok, new_stride_head, cu_seqlens_new, cache_pos,
                    num_seqs, max_new, k_cache, v_cache, kv_stride_b, kv_stride_head,
-                   kv_stride_tok, k_scale, v_scale, max_ctx, num_kv_heads, head_dim, stream);
+                   kv_stride_tok, k_scale, v_scale, nullptr, 0, 0, max_ctx, num_kv_heads, head_dim,
+                   stream);
+}
+
+int sink_attn_kv_append_paged(const void* k_new, const void* v_new, int64_t new_stride_tok,
+                              int64_t new_stride_head, const int32_t* cu_seqlens_new,
+                              const int32_t* cache_pos, int32_t num_seqs, int32_t max_new,
+                              void* k_pages, void* v_pages, int64_t page_stride,
+                              int64_t kv_stride_head, int64_t kv_stride_tok, int32_t page_size,
+                              const int32_t* block_tables, int64_t bt_stride,
+                              int32_t pages_per_seq, const float* k_scale, const float* v_scale,
+                              int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  g_err[0] = '\0';
+  if ((k_scale == nullptr) != (v_scale == nullptr))
+    return fail(SINK_ATTN_EINVAL, "k_scale and v_scale must both be given or both be null");
+  if (page_size <= 0) return fail(SINK_ATTN_EINVAL, "page_size must be a power of two in [16, 2^20] (got %d)", page_size);
+  if (pages_per_seq < 0) return fail(SINK_ATTN_EINVAL, "pages_per_seq must be >= 0");
+  const int64_t max_ctx = static_cast<int64_t>(pages_per_seq) * page_size;
+  if (max_ctx > 0x7fffffff) return fail(SINK_ATTN_EUNSUPPORTED, "pages_per_seq * page_size exceeds 2^31");
+  return kv_append(k_new, v_new, new_stride_tok, new_stride_head, cu_seqlens_new, cache_pos,
+                   num_seqs, max_new, k_pages, v_pages, page_stride, kv_stride_head,
+                   kv_stride_tok, k_scale, v_scale, block_tables, bt_stride, page_size,
+                   static_cast<int32_t>(max_ctx), num_kv_heads, head_dim, stream);
 }
 
 }  // extern "C"

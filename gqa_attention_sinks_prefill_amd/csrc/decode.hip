@@ -95,7 +95,10 @@ constexpr int decode_lds1_elems() {
 // F8: the caches hold FP8 E4M3 codes with a dequantization scale per KV head;
 // the codes convert exactly to bf16 for the MFMAs, k_scale joins the softmax
 // scale and v_scale the final division by d.
-template <int D, int CB, int W, bool F8>
+// PG: the caches are pages [num_pages, Hkv, page_size, D] reached through a
+// block table (page_size a power of two >= 16, so a 16-key block never
+// straddles pages): each 16-key block gets its own buffer resource.
+template <int D, int CB, int W, bool F8, bool PG>
 __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint16_t* v_lds0,
                                             uint16_t* v_lds1) {
   constexpr int DC = D / 8;                  // 16-byte chunks per bf16 row
@@ -189,13 +192,46 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
   const float qk_scale = F8 ? a.scale_log2 * a.k_scale[g] : a.scale_log2;
   const float out_scale = F8 ? a.v_scale[g] : 1.f;
 
-  // K / V of this chunk through buffer resources (loads past its end read 0)
+  // K / V of this chunk through buffer resources (loads past its end read 0):
+  // one over the chunk for contiguous caches, one per 16-key block for pages
   constexpr int EB = F8 ? 1 : 2;             // bytes per cached element
   const int stb = (int)(a.kv_st * EB);       // bytes per cached token
   const int64_t base = ((int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh + (int64_t)lo * a.kv_st) * EB;
   const int nbytes = n > 0 ? (n - 1) * stb + RB : 0;
-  const auto krs = make_rsrc(static_cast<const char*>(a.k_cache) + base, nbytes);
-  const auto vrs = make_rsrc(static_cast<const char*>(a.v_cache) + base, nbytes);
+  const auto krs = make_rsrc(static_cast<const char*>(a.k_cache) + (PG ? 0 : base), PG ? 0 : nbytes);
+  const auto vrs = make_rsrc(static_cast<const char*>(a.v_cache) + (PG ? 0 : base), PG ? 0 : nbytes);
+  // pages: the chunk's block-table entries, lane l holding entry l + 64r past
+  // its first page (at most 256 entries, checked on the host)
+  int pidx[4] = {0, 0, 0, 0};
+  int first_page = 0;
+  if constexpr (PG) {
+    first_page = lo >> a.page_shift;
+    if (n > 0) {
+      const int last_page = (lo + n - 1) >> a.page_shift;
+      const int32_t* bt = a.block_tables + (int64_t)b * a.bt_stride;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = first_page + lane + 64 * r;
+        pidx[r] = e <= last_page ? bt[e] : 0;
+      }
+    }
+  }
+  // Buffer resource of the 16-key block starting key16 keys into the chunk.
+  auto block_rsrc = [&](const void* cache, int key16) {
+    const int kabs = lo + key16;
+    const int e = __builtin_amdgcn_readfirstlane((kabs >> a.page_shift) - first_page);
+    int page;
+    switch (e >> 6) {
+      case 0: page = __builtin_amdgcn_readlane(pidx[0], e & 63); break;
+      case 1: page = __builtin_amdgcn_readlane(pidx[1], e & 63); break;
+      case 2: page = __builtin_amdgcn_readlane(pidx[2], e & 63); break;
+      default: page = __builtin_amdgcn_readlane(pidx[3], e & 63); break;
+    }
+    const int slot = kabs & ((1 << a.page_shift) - 1);
+    const int valid = min(16, len - kabs);
+    const int64_t off = ((int64_t)page * a.kv_sp + (int64_t)g * a.kv_sh + (int64_t)slot * a.kv_st) * EB;
+    return make_rsrc(static_cast<const char*>(cache) + off, valid > 0 ? (valid - 1) * stb + RB : 0);
+  };
 
   // K fragment kb (16 keys): lane holds key kb*16 + col; bf16: load cc is
   // d = 32cc + 8lgrp .. +7; FP8: load i is d = 64i + 16lgrp .. +15
@@ -232,16 +268,34 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
   auto load_k = [&](int st, u32x4_t (&kf)[4][NKL]) {
     const int off = st * kSub * stb;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      if constexpr (PG) {
+        const auto rs = block_rsrc(a.k_cache, st * kSub + 16 * kb);
 #pragma unroll
-      for (int i = 0; i < NKL; ++i) kf[kb][i] = buffer_load16<kNonTemporal>(krs, k_off[i] + kb * 16 * stb + off);
+        for (int i = 0; i < NKL; ++i) kf[kb][i] = buffer_load16<kNonTemporal>(rs, k_off[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NKL; ++i) kf[kb][i] = buffer_load16<kNonTemporal>(krs, k_off[i] + kb * 16 * stb + off);
+      }
+    }
   };
   // Buffer numbers are compile-time constants (std::integral_constant).
   auto dma_v = [&](int st, auto buf) {
     const int off = st * kSub * stb;
     uint16_t* dst = (decltype(buf)::value ? v_lds1 : v_lds0) + wave * TILE;
+    if constexpr (PG) {
+      constexpr int RPI = 1024 / RB;         // rows per copy instruction: within one 16-key block
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) buffer_load16_lds<kNonTemporal>(vrs, dst + i * 512, v_goff[i] + off);
+      for (int kb = 0; kb < 4; ++kb) {
+        const auto rs = block_rsrc(a.v_cache, st * kSub + 16 * kb);
+#pragma unroll
+        for (int i = kb * 16 / RPI; i < (kb + 1) * 16 / RPI; ++i)
+          buffer_load16_lds<kNonTemporal>(rs, dst + i * 512, v_goff[i] - 16 * kb * stb);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NDMA; ++i) buffer_load16_lds<kNonTemporal>(vrs, dst + i * 512, v_goff[i] + off);
+    }
   };
   // One 64-key sub-tile: every K operand and every V^T operand feeds the CB
   // column blocks' MFMAs.
@@ -451,11 +505,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
 // One workgroup per unit.  head_dim 64 with up to 2 column blocks runs 2 waves
 // per SIMD (16 KB of LDS per wave); wider blocks and head_dim 128 need the
 // registers of 1 wave per SIMD.
-template <int D, int CB, int W, bool F8>
+template <int D, int CB, int W, bool F8, bool PG>
 __global__ __launch_bounds__(64 * W, (D == 64 && CB <= 2) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t v_lds0[decode_lds0_elems<D, CB, W, F8>()];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds1[decode_lds1_elems<D, CB, W, F8>()];
-  decode_unit<D, CB, W, F8>(a, blockIdx.x, v_lds0, v_lds1);
+  decode_unit<D, CB, W, F8, PG>(a, blockIdx.x, v_lds0, v_lds1);
 }
 
 // Wave-wide reductions (64 lanes) for the merge.
@@ -562,37 +616,43 @@ int decode_waves_per_unit(int64_t num_units, int head_dim, int column_blocks) {
   return num_units >= simds ? 1 : (2 * num_units >= simds ? 2 : 4);
 }
 
-template <int D, int CB, bool F8>
+template <int D, int CB, bool F8, bool PG>
 hipError_t launch_decode_cb(const DecodeArgs& a, int64_t num_units, int waves, hipStream_t stream) {
   const dim3 grid((unsigned)num_units);
   switch (waves) {
-    case 1: hipLaunchKernelGGL((decode_split_kernel<D, CB, 1, F8>), grid, dim3(64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_split_kernel<D, CB, 2, F8>), grid, dim3(128), 0, stream, a); break;
-    default: hipLaunchKernelGGL((decode_split_kernel<D, CB, 4, F8>), grid, dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((decode_split_kernel<D, CB, 1, F8, PG>), grid, dim3(64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<D, CB, 2, F8, PG>), grid, dim3(128), 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_split_kernel<D, CB, 4, F8, PG>), grid, dim3(256), 0, stream, a); break;
   }
   return hipGetLastError();
 }
 
-template <int D, bool F8>
+template <int D, bool F8, bool PG>
 hipError_t launch_decode_d(const DecodeArgs& a, int64_t num_units, hipStream_t stream) {
   const int cb = decode_column_blocks(a.ncols, D);
   const int waves = decode_waves_per_unit(num_units, D, cb);
   switch (cb) {
-    case 1: return launch_decode_cb<D, 1, F8>(a, num_units, waves, stream);
-    case 2: return launch_decode_cb<D, 2, F8>(a, num_units, waves, stream);
+    case 1: return launch_decode_cb<D, 1, F8, PG>(a, num_units, waves, stream);
+    case 2: return launch_decode_cb<D, 2, F8, PG>(a, num_units, waves, stream);
     default:
-      if constexpr (D == 64) return launch_decode_cb<D, 4, F8>(a, num_units, waves, stream);
+      if constexpr (D == 64) return launch_decode_cb<D, 4, F8, PG>(a, num_units, waves, stream);
       return hipErrorInvalidValue;
   }
 }
 
+template <bool F8, bool PG>
+hipError_t launch_decode_kind(const DecodeArgs& a, int head_dim, int64_t num_blocks, hipStream_t stream) {
+  return head_dim == 64 ? launch_decode_d<64, F8, PG>(a, num_blocks, stream)
+                        : launch_decode_d<128, F8, PG>(a, num_blocks, stream);
+}
+
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,
                                hipStream_t stream) {
-  if (a.k_scale != nullptr)
-    return head_dim == 64 ? launch_decode_d<64, true>(a, num_blocks, stream)
-                          : launch_decode_d<128, true>(a, num_blocks, stream);
-  return head_dim == 64 ? launch_decode_d<64, false>(a, num_blocks, stream)
-                        : launch_decode_d<128, false>(a, num_blocks, stream);
+  const bool f8 = a.k_scale != nullptr, pg = a.block_tables != nullptr;
+  if (f8) return pg ? launch_decode_kind<true, true>(a, head_dim, num_blocks, stream)
+                    : launch_decode_kind<true, false>(a, head_dim, num_blocks, stream);
+  return pg ? launch_decode_kind<false, true>(a, head_dim, num_blocks, stream)
+            : launch_decode_kind<false, false>(a, head_dim, num_blocks, stream);
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {

@@ -50,7 +50,7 @@ __device__ __forceinline__ u32x2_t quantize8(const u32x4_t& bf, float inv) {
   return r;
 }
 
-template <int D, bool F8>
+template <int D, bool F8, bool PG>
 __global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
   constexpr int DC = D / 8;                   // 16-byte chunks per bf16 token row
   constexpr int TPP = kThreads / DC;          // tokens per pass
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
   const int64_t pos = a.cache_pos[b];
   const int c = threadIdx.x % DC;
   const int t0 = tb * TB + threadIdx.x / DC;
-  const int64_t cache_row = (int64_t)b * a.kv_sb + (int64_t)g * a.kv_sh;
+  const int64_t cache_row = (PG ? 0 : (int64_t)b * a.kv_sb) + (int64_t)g * a.kv_sh;
 
   u32x4_t kr[kPasses], vr[kPasses];
   bool ok[kPasses];
@@ -88,7 +88,14 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(KvAppendArgs a) {
 #pragma unroll
   for (int p = 0; p < kPasses; ++p) {
     if (ok[p]) {
-      const int64_t dst = cache_row + (pos + t0 + p * TPP) * a.kv_st + 8 * c;
+      const int64_t slot = pos + t0 + p * TPP;
+      int64_t dst;
+      if constexpr (PG) {   // page block_tables[b][slot / P], row slot % P
+        const int32_t page = a.block_tables[(int64_t)b * a.bt_stride + (slot >> a.page_shift)];
+        dst = (int64_t)page * a.kv_sb + cache_row + (slot & ((1 << a.page_shift) - 1)) * a.kv_st + 8 * c;
+      } else {
+        dst = cache_row + slot * a.kv_st + 8 * c;
+      }
       if constexpr (F8) {
         *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.k_cache) + dst) = quantize8(kr[p], k_inv);
         *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.v_cache) + dst) = quantize8(vr[p], v_inv);
@@ -107,13 +114,16 @@ int kv_append_tokens_per_block(int head_dim) { return kThreads / (head_dim / 8) 
 hipError_t launch_kv_append(const KvAppendArgs& a, int head_dim, int64_t num_blocks,
                             hipStream_t stream) {
   const dim3 grid((unsigned)num_blocks), block(kThreads);
-  const bool f8 = a.k_scale != nullptr;
-  if (head_dim == 64) {
-    if (f8) hipLaunchKernelGGL((kv_append_kernel<64, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((kv_append_kernel<64, false>), grid, block, 0, stream, a);
-  } else {
-    if (f8) hipLaunchKernelGGL((kv_append_kernel<128, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((kv_append_kernel<128, false>), grid, block, 0, stream, a);
+  const int kind = (a.k_scale != nullptr ? 1 : 0) + (a.block_tables != nullptr ? 2 : 0);
+  switch (kind + (head_dim == 64 ? 0 : 4)) {
+    case 0: hipLaunchKernelGGL((kv_append_kernel<64, false, false>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((kv_append_kernel<64, true, false>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((kv_append_kernel<64, false, true>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((kv_append_kernel<64, true, true>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((kv_append_kernel<128, false, false>), grid, block, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((kv_append_kernel<128, true, false>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((kv_append_kernel<128, false, true>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((kv_append_kernel<128, true, true>), grid, block, 0, stream, a); break;
   }
   return hipGetLastError();
 }

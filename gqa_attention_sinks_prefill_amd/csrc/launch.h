@@ -36,6 +36,10 @@ struct DecodeArgs {
   int64_t kv_sb, kv_sh, kv_st;  // in elements
   const float* k_scale;      // FP8 caches: dequantization scale per KV head (else null)
   const float* v_scale;
+  const int32_t* block_tables;  // paged caches: [batch, >= pages per request] (else null)
+  int64_t bt_stride;         // elements between block-table rows
+  int64_t kv_sp;             // paged caches: elements between pages (kv_sb unused)
+  int32_t page_shift;        // log2(page_size)
   const int32_t* seq_lens;
   const float* sinks;
   float* part_o;
@@ -76,7 +80,10 @@ struct KvAppendArgs {
   int64_t kv_sb, kv_sh, kv_st;  // in elements
   const float* k_scale;     // FP8 caches: dequantization scale per KV head (else null)
   const float* v_scale;
-  int32_t max_ctx;
+  const int32_t* block_tables;  // paged caches (else null); kv_sb is then the page stride
+  int64_t bt_stride;
+  int32_t page_shift;      // log2(page_size)
+  int32_t max_ctx;         // slots per request (pages: table width * page_size)
   int32_t num_kv_heads;
   int32_t token_blocks;    // ceil(max_new / tokens per workgroup)
 };

@@ -279,6 +279,55 @@ int sink_attn_kv_append_fp8(const void* k_new, const void* v_new, int64_t new_st
                             const float* v_scale, int32_t max_ctx, int32_t num_kv_heads,
                             int32_t head_dim, void* stream);
 
+/*
+ * Paged (block-table) KV cache.  The pages keep each request's cache in HND
+ * order ("Hosting Qwen on Blackwell", section "Deployment on GB200 NVL72");
+ * a serving engine holds it in fixed-size pages instead of one contiguous
+ * slab per request (not on the pages; reading: HND inside each page).
+ *   k_pages, v_pages: [num_pages, Hkv, page_size, D], bf16 -- or FP8 E4M3
+ *       codes when k_scale and v_scale are given (both or neither) -- with
+ *       element strides page_stride, kv_stride_head, kv_stride_tok (d
+ *       unit-stride; multiples of 8 bf16 / 16 FP8 elements).
+ *   page_size: tokens per page, a power of two in [16, 2^20].
+ *   block_tables [batch, pages_per_seq] int32, device, row stride bt_stride:
+ *       request b's token j lives in page block_tables[b*bt_stride +
+ *       j / page_size], row j % page_size.  Precondition: every entry a
+ *       request's length reaches is a valid page index, and seq_lens[b] <=
+ *       pages_per_seq * page_size (unchecked device values).
+ * sink_attn_decode_paged_split: sink_attn_decode_multi_split (or its FP8
+ * form) over such pages -- the same chunk states, same shapes; max_ctx is
+ * pages_per_seq * page_size.  Chunks may span at most 255 pages
+ * (split_size <= 254 * page_size, else SINK_ATTN_EUNSUPPORTED).
+ */
+int sink_attn_decode_paged_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                                 int64_t q_stride_head, int32_t q_len, const void* k_pages,
+                                 const void* v_pages, int64_t page_stride, int64_t kv_stride_head,
+                                 int64_t kv_stride_tok, int32_t page_size,
+                                 const int32_t* block_tables, int64_t bt_stride,
+                                 int32_t pages_per_seq, const float* k_scale, const float* v_scale,
+                                 const int32_t* seq_lens, int32_t batch, const float* sinks,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 float scale, int32_t split_size, int32_t num_splits,
+                                 float* part_o, float* part_m, float* part_d, void* stream);
+
+/*
+ * sink_attn_kv_append_paged: sink_attn_kv_append (a copy into bf16 pages) or
+ * sink_attn_kv_append_fp8 (quantizing into FP8 pages, when the scales are
+ * given) through a block table: new token t of request b goes to logical slot
+ * cache_pos[b] + t, i.e. page block_tables[b*bt_stride + slot / page_size],
+ * row slot % page_size; slots at or past pages_per_seq * page_size are
+ * dropped.  Layout, strides and preconditions as for
+ * sink_attn_decode_paged_split.
+ */
+int sink_attn_kv_append_paged(const void* k_new, const void* v_new, int64_t new_stride_tok,
+                              int64_t new_stride_head, const int32_t* cu_seqlens_new,
+                              const int32_t* cache_pos, int32_t num_seqs, int32_t max_new,
+                              void* k_pages, void* v_pages, int64_t page_stride,
+                              int64_t kv_stride_head, int64_t kv_stride_tok, int32_t page_size,
+                              const int32_t* block_tables, int64_t bt_stride,
+                              int32_t pages_per_seq, const float* k_scale, const float* v_scale,
+                              int32_t num_kv_heads, int32_t head_dim, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  The pointer
  * stays valid until the next call into the library on the same thread. */
 const char* sink_attn_last_error(void);

@@ -289,6 +289,79 @@ def test_kv_append_fp8_empty_work_is_a_noop():
     assert _kv_append_fp8(num_seqs=0, kn=None)[0] == 0
 
 
+def _decode_paged(**kw):
+    a = dict(q=16, q_sb=4 * 4096, q_st=4096, q_sh=64, q_len=1, k=16, v=16, sp=8 * 16 * 64,
+             kv_sh=16 * 64, kv_st=64, ps=16, bt=4, bt_st=64, pps=64, ks=None, vs=None, lens=4,
+             batch=4, sinks=4, hq=64, hkv=8, d=64, scale=0.125, split=256, nsplit=4, po=4, pm=4,
+             pd=4)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_decode_paged_split(
+        a["q"], a["q_sb"], a["q_st"], a["q_sh"], a["q_len"], a["k"], a["v"], a["sp"], a["kv_sh"],
+        a["kv_st"], a["ps"], a["bt"], a["bt_st"], a["pps"], a["ks"], a["vs"], a["lens"],
+        a["batch"], a["sinks"], a["hq"], a["hkv"], a["d"], a["scale"], a["split"], a["nsplit"],
+        a["po"], a["pm"], a["pd"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ps=24), -1, "power of two"),
+    (dict(ps=8), -1, "power of two"),
+    (dict(ps=0), -1, "power of two"),
+    (dict(bt=None), -1, "null"),
+    (dict(bt=6), -1, "aligned"),
+    (dict(bt_st=-1), -1, ">= 0"),
+    (dict(pps=-1), -1, ">= 0"),
+    (dict(pps=1 << 27, ps=32), -2, "2^31"),
+    (dict(ks=4), -1, "both"),
+    (dict(split=8192, nsplit=1, ps=16), -2, "255 pages"),
+    (dict(nsplit=2), -1, "cover"),
+    (dict(kv_st=68), -1, "multiples of 8"),
+    (dict(ks=4, vs=8, kv_st=72), -1, "multiples of 16"),
+    (dict(d=32), -2, "head_dim"),
+])
+def test_decode_paged_split_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _decode_paged(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_decode_paged_split_empty_batch_is_a_noop():
+    assert _decode_paged(batch=0, q=None)[0] == 0
+
+
+def _kv_append_paged(**kw):
+    a = dict(kn=16, vn=32, n_st=512, n_sh=64, cu=4, pos=8, num_seqs=2, max_new=100, kc=48,
+             vc=64, sp=8 * 16 * 64, kv_sh=16 * 64, kv_st=64, ps=16, bt=4, bt_st=64, pps=64,
+             ks=None, vs=None, hkv=8, d=64)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_kv_append_paged(a["kn"], a["vn"], a["n_st"], a["n_sh"], a["cu"], a["pos"],
+                                       a["num_seqs"], a["max_new"], a["kc"], a["vc"], a["sp"],
+                                       a["kv_sh"], a["kv_st"], a["ps"], a["bt"], a["bt_st"],
+                                       a["pps"], a["ks"], a["vs"], a["hkv"], a["d"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ps=48), -1, "power of two"),
+    (dict(bt=None), -1, "null"),
+    (dict(bt=2), -1, "aligned"),
+    (dict(vs=8), -1, "both"),
+    (dict(kn=None), -1, "null"),
+    (dict(d=96), -2, "head_dim"),
+])
+def test_kv_append_paged_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _kv_append_paged(**kw)
+    assert rc == code
+    assert needle in msg
+
+
+def test_kv_append_paged_empty_work_is_a_noop():
+    assert _kv_append_paged(num_seqs=0, kn=None)[0] == 0
+    assert _kv_append_paged(pps=0)[0] == 0
+
+
 def _merge(**kw):
     a = dict(po=4, pm=4, pd=4, batch=2, hq=8, ns=4, d=64, o=16, o_sb=512, o_sh=64, lse=None)
     a.update(kw)

@@ -704,3 +704,149 @@ def test_kv_append_fp8_then_decode():
     o_ref, lse_ref, _ = _fp8_ref(inp)
     assert_close(out.reshape(-1, D), o_ref, what="fp8 append then decode")
     assert_lse_close(lse.reshape(-1), lse_ref, what="fp8 append then decode lse")
+
+
+# ------------------------------------------------------------- paged caches --
+def _to_pages(logical, P, g, extra_pages=7, poison=None):
+    """Scatter logical caches [B, Hkv, L, D] into pages [num_pages, Hkv, P, D]
+    under a random permutation; unreferenced pages and the tail of the last
+    page of each request hold `poison`.  Returns (pages, block_tables [B, L/P])."""
+    B, Hkv, L, D = logical.shape
+    per = -(-L // P)
+    num_pages = B * per + extra_pages
+    perm = torch.randperm(num_pages, generator=g)[:B * per].view(B, per).to(torch.int32)
+    pages = torch.full((num_pages, Hkv, P, D), poison, dtype=logical.dtype) if poison is not None \
+        else torch.zeros((num_pages, Hkv, P, D), dtype=logical.dtype)
+    for b in range(B):
+        for p in range(per):
+            blk = logical[b, :, p * P:(p + 1) * P]
+            pages[int(perm[b, p]), :, :blk.shape[1]] = blk
+    return pages, perm
+
+
+def _paged_case(lens, q_len, Hq, Hkv, D, P, fp8, seed, max_ctx):
+    if fp8:
+        cfg = wl.DecodeConfig("pg8", len(lens), None, (1, 1), max_ctx, Hq, Hkv, D, (-4.0, 4.0),
+                              split_size=64, seed=seed, edge_sinks={0: float("-inf"), Hq - 1: 20.0},
+                              q_len=q_len)
+        inp = wl.fp8_decode_inputs(cfg, lens=lens)
+        poison = 0x7F
+    else:
+        cfg = wl.DecodeConfig("pg", len(lens), None, (1, 1), max_ctx, Hq, Hkv, D, (-4.0, 4.0),
+                              split_size=64, seed=seed, edge_sinks={0: float("-inf"), Hq - 1: 20.0},
+                              q_len=q_len)
+        inp = wl.decode_inputs(cfg, lens=lens)
+        poison = float("nan")
+    g = torch.Generator().manual_seed(seed)
+    kp, bt = _to_pages(inp["k_cache"], P, g, poison=poison)
+    vp = torch.full_like(kp, poison) if fp8 else torch.full_like(kp, float("nan"))
+    for b in range(bt.shape[0]):
+        for p in range(bt.shape[1]):
+            blk = inp["v_cache"][b, :, p * P:(p + 1) * P]
+            vp[int(bt[b, p]), :, :blk.shape[1]] = blk
+    return inp, kp, vp, bt
+
+
+def _paged_gpu(inp, kp, vp, bt, split, fp8):
+    q = _q4(inp["q"]).to(DEV)
+    B, q_len, Hq, D = q.shape
+    ns = -(-bt.shape[1] * kp.shape[2] // split)
+    po = torch.full((B, q_len, Hq, ns, D), float("nan"), device=DEV)
+    pm = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    pd = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    out = torch.full((B, q_len, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, q_len, Hq), float("nan"), device=DEV)
+    sc = dict(k_scale=inp["k_scale"].to(DEV), v_scale=inp["v_scale"].to(DEV)) if fp8 else {}
+    sa.sink_attn_decode_paged(q, kp.to(DEV), vp.to(DEV), bt.to(DEV), inp["seq_lens"].to(DEV),
+                              inp["sinks"].to(DEV), split, ns, out=out, lse=lse,
+                              partials=(po, pm, pd), **sc)
+    torch.cuda.synchronize()
+    return out, lse, (po, pm, pd)
+
+
+def _paged_ref(inp, kp, vp, bt, P, fp8, rows=None):
+    sc = dict(k_scale=inp["k_scale"].numpy(), v_scale=inp["v_scale"].numpy()) if fp8 else {}
+    return oracle.decode_multi_paged(_q4(inp["q"]), kp, vp, bt, P, inp["seq_lens"],
+                                     inp["sinks"], rows=rows, **sc)
+
+
+@pytest.mark.parametrize("P,fp8,q_len,D", [(16, False, 1, 64), (16, True, 1, 64),
+                                           (64, False, 3, 64), (256, True, 2, 64),
+                                           (16, False, 1, 128), (32, True, 4, 128)])
+def test_decode_paged_all_rows(P, fp8, q_len, D):
+    """Pages under a random table against the oracle on every row; lengths on
+    page, sub-tile and chunk edges; unreferenced pages and page tails hold NaN
+    (bf16) or the NaN code (FP8)."""
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 255, 256, 257, 700]
+    max_ctx = -(-704 // P) * P
+    inp, kp, vp, bt = _paged_case(lens, q_len, 64, 8, D, P, fp8, 130 + P + q_len + D, max_ctx)
+    out, lse, _ = _paged_gpu(inp, kp, vp, bt, 256, fp8)
+    o_ref, lse_ref, _ = _paged_ref(inp, kp, vp, bt, P, fp8)
+    what = f"paged decode P={P} fp8={fp8} q_len={q_len} D={D}"
+    assert_close(out.reshape(-1, D), o_ref, what=what)
+    assert_lse_close(lse.reshape(-1), lse_ref, what=f"{what} lse")
+
+
+@pytest.mark.parametrize("B,q_len,fp8", [(128, 1, False), (128, 3, True), (24, 3, False)])
+def test_decode_paged_work_splits(B, q_len, fp8):
+    """Each way waves share a chunk (four, one, two) over 16-token pages."""
+    lens = [_EDGE_LENS[(3 * i) % len(_EDGE_LENS)] for i in range(B)]
+    inp, kp, vp, bt = _paged_case(lens, q_len, 64, 8, 64, 16, fp8, 140 + B + q_len, 512)
+    out, lse, (po, pm, pd) = _paged_gpu(inp, kp, vp, bt, 64, fp8)
+    o_ref, lse_ref, _ = _paged_ref(inp, kp, vp, bt, 16, fp8)
+    assert_close(out.reshape(-1, 64), o_ref, what=f"paged decode B={B} q_len={q_len}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what=f"paged decode B={B} lse")
+    assert not torch.isnan(po).any() and not torch.isnan(pm).any()
+
+
+def test_decode_paged_full_config_sampled_rows():
+    """64 requests x 8192 tokens in 16-token pages under a random table."""
+    cfg = wl.SPLIT_DECODE
+    inp = wl.decode_inputs(cfg)
+    g = torch.Generator().manual_seed(150)
+    kp, bt = _to_pages(inp["k_cache"], 16, g, extra_pages=0)
+    vp = torch.empty_like(kp)
+    for b in range(bt.shape[0]):
+        for p in range(bt.shape[1]):
+            vp[int(bt[b, p])] = inp["v_cache"][b, :, p * 16:(p + 1) * 16]
+    out, lse, _ = _paged_gpu(inp, kp, vp, bt, cfg.split_size, False)
+    rows = sorted({(int(torch.randint(cfg.batch, (1,), generator=g)), 0,
+                    int(torch.randint(cfg.num_q_heads, (1,), generator=g))) for _ in range(64)})
+    o_ref, lse_ref, _ = oracle.decode_multi(_q4(inp["q"]), inp["k_cache"], inp["v_cache"],
+                                            inp["seq_lens"], inp["sinks"], rows=rows)
+    idx = torch.tensor(rows)
+    assert_close(out.cpu()[idx[:, 0], 0, idx[:, 2]], o_ref, what="paged decode full config")
+    assert_lse_close(lse.cpu()[idx[:, 0], 0, idx[:, 2]], lse_ref, what="paged decode full config lse")
+
+
+@pytest.mark.parametrize("fp8,P,D", [(False, 16, 64), (True, 16, 64), (False, 64, 128), (True, 32, 128)])
+def test_kv_append_paged_bitwise(fp8, P, D):
+    """Append through a random block table against the oracle, element for
+    element (codes for FP8); slots past the table's capacity are dropped."""
+    counts, Hkv, width = [3, 0, 130, 64, 90], 4, 8          # capacity 8 pages per request
+    d = wl.kv_append_inputs(counts, width * P, Hkv, D, seed=160 + P + D,
+                            pos=[0, 5, P + 3, width * P - 64, width * P - 50])
+    g = torch.Generator().manual_seed(161)
+    B = len(counts)
+    num_pages = B * width + 3
+    bt = torch.randperm(num_pages, generator=g)[:B * width].view(B, width).to(torch.int32)
+    if fp8:
+        kp = torch.randint(0, 256, (num_pages, Hkv, P, D), generator=g, dtype=torch.uint8)
+        vp = torch.randint(0, 256, (num_pages, Hkv, P, D), generator=g, dtype=torch.uint8)
+        ks = torch.empty(Hkv).uniform_(0.002, 0.02, generator=g)
+        vs = torch.empty(Hkv).uniform_(0.002, 0.02, generator=g)
+        sc = dict(k_scale=ks.numpy(), v_scale=vs.numpy())
+        sg = dict(k_scale=ks.to(DEV), v_scale=vs.to(DEV))
+    else:
+        kp = torch.randn(num_pages, Hkv, P, D, generator=g).to(torch.bfloat16)
+        vp = torch.randn(num_pages, Hkv, P, D, generator=g).to(torch.bfloat16)
+        sc, sg = {}, {}
+    ko, vo = oracle.kv_append_paged(d["k_new"], d["v_new"], d["cu_seqlens_new"], d["cache_pos"],
+                                    kp, vp, bt, P, **sc)
+    kg, vg = kp.to(DEV), vp.to(DEV)
+    sa.sink_attn_kv_append_paged(d["k_new"].to(DEV), d["v_new"].to(DEV),
+                                 d["cu_seqlens_new"].to(DEV), d["cache_pos"].to(DEV), kg, vg,
+                                 bt.to(DEV), **sg)
+    torch.cuda.synchronize()
+    view = (lambda t: t) if fp8 else (lambda t: t.view(torch.int16))
+    assert torch.equal(view(kg.cpu()), view(ko)) and torch.equal(view(vg.cpu()), view(vo))
