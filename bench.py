@@ -24,7 +24,8 @@ After the timed steps (not part of them): `hbm_read_reference` times a plain
 streaming-read kernel (libhbmprobe.so) and `decode.frac_of_measured_read`
 relates the decode to it; `extra` holds the other workloads' lines -- the
 head_dim 128 varlen prefill, chunked prefill, multi-token decode, decode over
-FP8 caches, KV-cache append and the ragged long-context decode at B = 1, 8,
+FP8 caches and over 16-token pages, KV-cache append and the ragged
+long-context decode at B = 1, 8,
 32, 128 (B < 32 is launch / latency bound and flagged so).
 """
 from __future__ import annotations
@@ -278,6 +279,59 @@ def fp8_decode_measurement(dev, stream, reps: int):
             "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def paged_decode_measurement(dev, stream, reps: int, page_size: int = 16):
+    """Decode over a paged bf16 cache: the split-decode shape (64 x 8192, 64 / 8
+    heads, d 64, split 1024 + merge) in 16-token pages under a random block
+    table (seeded), event-timed; GB/s of K/V bytes read."""
+    cfg = wl.SPLIT_DECODE
+    inp = wl.decode_inputs(cfg)
+    B, Hkv, L, D = inp["k_cache"].shape
+    per = L // page_size
+    g = torch.Generator().manual_seed(9)
+    perm = torch.randperm(B * per, generator=g).view(B, per).to(torch.int32)
+    # page p of request b holds its tokens p*P .. p*P+P-1 (one scatter on the GPU)
+    kc, vc = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    kp = torch.empty(B * per, Hkv, page_size, D, dtype=torch.bfloat16, device=dev)
+    vp = torch.empty_like(kp)
+    src_k = kc.view(B, Hkv, per, page_size, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page_size, D)
+    src_v = vc.view(B, Hkv, per, page_size, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page_size, D)
+    idx = perm.view(-1).to(dev).long()
+    kp[idx] = src_k
+    vp[idx] = src_v
+    del kc, vc, src_k, src_v
+    bt = perm.to(dev)
+    q, lens, sinks = inp["q"].to(dev), inp["seq_lens"].to(dev), inp["sinks"].to(dev)
+    Hq = q.shape[1]
+    ns = cfg.num_splits
+    po = torch.empty(B, 1, Hq, ns, D, device=dev)
+    pm = torch.empty(B, 1, Hq, ns, device=dev)
+    pd = torch.empty(B, 1, Hq, ns, device=dev)
+    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    run = lambda: sa.sink_attn_decode_paged(q, kp, vp, bt, lens, sinks, cfg.split_size, ns,
+                                            scale=cfg.scale, out=out, partials=(po, pm, pd),
+                                            stream=stream)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+         for _ in range(reps)]
+    for a, b in e:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
+    kv = wl.decode_kv_bytes(inp["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
+    gbs = kv / (ms * 1e-3) / 1e9
+    del kp, vp
+    torch.cuda.empty_cache()
+    return {"workload": f"paged_decode_b64_ctx8192_page{page_size}_h64kv8_d64_split1024",
+            "value": round(gbs, 1), "unit": "GB/s",
+            "metric": "paged decode KV GB/s (split + merge)", "mean_ms": round(ms, 4),
+            "algorithmic_bytes_per_step": kv,
+            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def hbm_read_reference(dev, stream, reps: int = 10):
     """GB/s of a plain streaming-read kernel (libhbmprobe.so, built beside the
     library): 4 GiB read once per launch, each workgroup a contiguous slice,
@@ -487,6 +541,7 @@ def main():
                         chunked_prefill_measurement(dev, stream, max(3, args.steps // 2)),
                         multi_decode_measurement(dev, stream, max(3, args.steps // 2)),
                         fp8_decode_measurement(dev, stream, max(3, args.steps // 2)),
+                        paged_decode_measurement(dev, stream, max(3, args.steps // 2)),
                         kv_append_measurement(dev, stream, max(3, args.steps // 2))]
         res["extra"] += [ragged_decode_measurement(dev, stream, b, max(3, args.steps // 4))
                          for b in wl.RAGGED_BATCHES]
