@@ -76,6 +76,12 @@ int sink_attn_prefill_chunked(const void* q, int64_t q_stride_tok, int64_t q_str
       !stride_ok(k_stride_head) || !stride_ok(v_stride_tok) || !stride_ok(v_stride_head) ||
       !stride_ok(o_stride_tok) || !stride_ok(o_stride_head))
     return fail(SINK_ATTN_EINVAL, "strides must be non-negative multiples of 8 elements");
+  // one sequence's keys are addressed with 32-bit byte offsets (the key count
+  // of a chunked call is on the device; its bound is a documented precondition)
+  if (cu_seqlens_k == cu_seqlens_q &&
+      static_cast<int64_t>(max_seqlen) * (k_stride_tok > v_stride_tok ? k_stride_tok : v_stride_tok) * 2 >
+          0x7fffffffLL)
+    return fail(SINK_ATTN_EUNSUPPORTED, "max_seqlen * token stride spans more than 2 GiB");
 
   const int group = num_q_heads / num_kv_heads;
   const int hpw = sinkattn::prefill_heads_per_workgroup(group);

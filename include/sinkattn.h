@@ -70,7 +70,9 @@ extern "C" {
  *   sinks [Hq] fp32.
  *   cu_seqlens [num_seqs + 1] int32, device: sequence s owns packed tokens
  *       cu_seqlens[s] .. cu_seqlens[s+1]-1.  Precondition: cu_seqlens[0] = 0,
- *       non-decreasing, every length <= max_seqlen.
+ *       non-decreasing, every length <= max_seqlen.  One sequence's keys are
+ *       addressed with 32-bit byte offsets: max_seqlen * k_stride_tok * 2
+ *       (and the same for v) must stay below 2^31, else SINK_ATTN_EUNSUPPORTED.
  *   max_seqlen: host-side upper bound of the sequence lengths (sizes the grid).
  *   scale: softmax scale applied to q.k (1/sqrt(D) is usual); the sink is
  *       not scaled.
@@ -105,6 +107,8 @@ int sink_attn_prefill(const void* q, int64_t q_stride_tok, int64_t q_stride_head
  *       both start at 0 and are non-decreasing, every chunk length is at most
  *       max_seqlen_q and at most its sequence's key count; a sequence that
  *       breaks the last condition is skipped (its outputs are left unwritten).
+ *       Each sequence's key count times k_stride_tok * 2 (and v's) must stay
+ *       below 2^31 bytes (32-bit offsets; unchecked device values).
  *   lse: NULL, or fp32 [Tq, Hq] contiguous.
  *   Other arguments and errors as sink_attn_prefill.
  */

@@ -252,6 +252,14 @@ def test_decode_multi_split_fp8_empty_batch_is_a_noop():
     assert _decode_multi_fp8(batch=0, q=None)[0] == 0
 
 
+def test_prefill_sequence_span_must_fit_32_bits():
+    lib = sa.load_library()
+    # NHD keys with a 1M-element token stride: 4096 tokens span 8 GiB
+    rc = lib.sink_attn_prefill(16, 512, 64, 16, 1 << 20, 64, 16, 1 << 20, 64, 4, 4, 1, 4096, 8,
+                               8, 64, 0.125, 1, 16, 512, 64, None, None)
+    assert rc == -2 and "2 GiB" in lib.sink_attn_last_error().decode()
+
+
 def test_decode_split_size_times_stride_must_fit_32_bits():
     rc, msg = _decode_multi(kv_st=1 << 21, split=1024)
     assert rc == -2 and "2 GiB" in msg
