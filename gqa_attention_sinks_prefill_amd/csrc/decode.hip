@@ -36,6 +36,10 @@
 // W trades the merge across waves against parallelism inside a chunk: four
 // waves per chunk for one light column block; one wave per chunk, writing its
 // state directly, for heavier math when the chunks alone fill the SIMDs.
+// Two cache forms beyond bf16 per-request slabs share the kernel: FP8 E4M3
+// codes with a scale per KV head (converted exactly to bf16 in registers;
+// V through the 8-bit transposing read), and pages behind a block table (a
+// buffer resource per 16-key block).
 // merge_kernel: one wave per (b, h) row, lane = d; log-sum-exp weighted sum of
 // the chunk states, rounded to bf16.
 #include "device_common.h"
