@@ -36,7 +36,7 @@
 //     detected after the exponentials, so the vector ALU does per score one
 //     fma + exp2, half a bf16 pack and (head_dim 64) half a bf16 pair-add for
 //     the denominator; head_dim 128 sums the weights on the matrix pipe
-//     instead (a ones row times P^T).  o = O / d does not depend on m.
+//     instead (a 0/1 matrix times P^T on 16x16x32).  o = O / d does not depend on m.
 //   * Software pipeline: iteration j runs the QK^T MFMAs of tile j+1 next to
 //     the exponentials of tile j; with head_dim 64 also the P.V MFMAs of tile
 //     j-1 from operands held in registers, so that the matrix and vector
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
   constexpr int KT = BN * D;             // elements of one K or V tile
   constexpr int DMA = BN * DC / kThreads;   // 16-byte DMA slots per thread per tile
   constexpr bool kDeferPV = D == 64;        // P.V one tile behind (registers permitting)
-  // Tile weight sums on the matrix pipe (a ones row times P^T) where the
+  // Tile weight sums on the matrix pipe (a 0/1 matrix times P^T) where the
   // contractions leave it room (head_dim 128), else on the vector ALU.
   constexpr bool kSumOnMatrix = D == 128;
   // Separate arrays per buffer: the compiler then sees that the copies into
@@ -255,16 +255,22 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
 
   // Weights of a tile under the current stabiliser: pf = bf16(exp2(s*c2 - m)),
   // already in the P.V operand layout, and ts = this lane's share of their
-  // sum (the same bf16 values that enter P.V).  On the matrix pipe a ones row
-  // times P^T leaves the whole column sum in every accumulator element; only
+  // sum (the same bf16 values that enter P.V).  On the matrix pipe the P^T
+  // operand of a 16-key step is read as the B operand of a 16x16x32 MFMA
+  // (lane group q = l/16 supplies query (l%16) + 16(q%2), keys 8(q/2)..+7)
+  // against a 0/1 matrix whose row m is 1 on the groups with q%2 = (m/4)%2:
+  // every lane then receives the 16-key sum of its own query (half the matrix
+  // cycles and a quarter of the registers of a ones row on 32x32x16).  Only
   // the lower half of the lanes keeps it, so that lanes l and l^32 still add
   // up to the row's sum.
-  const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const u32x4_t ones16 = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)
+                             ? u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}
+                             : u32x4_t{0u, 0u, 0u, 0u};
   auto weights = [&](f32x16_t (&s)[QB][KB], u32x4_t (&pf)[QB][NU], float (&ts)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float t0 = 0.f, t1 = 0.f;
-      f32x16_t tm = {};
+      f32x4_t tm = {};
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         const int kb = u >> 1, base = 8 * (u & 1);
@@ -276,7 +282,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
         pf[qb][u][2] = pack_bf16x2(p[4], p[5]);
         pf[qb][u][3] = pack_bf16x2(p[6], p[7]);
         if constexpr (kSumOnMatrix) {
-          tm = mfma_32x32x16(ones, pf[qb][u], tm);
+          tm = mfma_16x16x32(ones16, pf[qb][u], tm);
         } else {
           t0 = add_bf16x2(pf[qb][u][0], t0);
           t1 = add_bf16x2(pf[qb][u][1], t1);
@@ -359,13 +365,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
     weights(s_cur, pf_cur, ts);
     if constexpr (kDeferPV) read_v(cur, vf_cur);
     // The stabiliser moves only when a lane's tile weights sum past
-    // kMaxTileSum (an overflow to inf included).  Until then every weight
+    // kMaxTileSum (an overflow to inf included, and the NaN that 0 * inf gives
+    // in the 0/1 matrix sum).  Until then every weight
     // stays below kMaxTileSum, O and the denominator share the same m, and
     // o = O / d is unchanged -- one wave-uniform branch per tile and no row
     // max.  A move rescales O after P.V of tile j-1 has entered it.
     bool big = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) big |= ts[qb] > kMaxTileSum;
+    for (int qb = 0; qb < QB; ++qb) big |= !(ts[qb] <= kMaxTileSum);
     if (__builtin_amdgcn_ballot_w64(big) != 0) restabilise(s_cur, pf_cur, ts);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lsum[qb] += ts[qb];
