@@ -116,12 +116,6 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2_t, r);
 }
 
-// acc + the two bf16 halves of `packed` (v_dot2 with a pair of ones).
-__device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
-                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
-}
 // Transposing 8-bit LDS read (ds_read_b64_tr_b8).  Within each group of 16
 // lanes, lane i receives byte (i & 7) of the 8-byte pieces addressed by lanes
 // 2k + (i >> 3), k = 0..7, as its bytes k = 0..7 (established by an in-bounds

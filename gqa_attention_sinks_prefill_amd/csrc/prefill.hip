@@ -34,9 +34,9 @@
 //     at the sink's logit and moves (to the running row max, rescaling O and
 //     the denominator) only when a tile's weights sum past kMaxTileSum --
 //     detected after the exponentials, so the vector ALU does per score one
-//     fma + exp2, half a bf16 pack and (head_dim 64) half a bf16 pair-add for
-//     the denominator; head_dim 128 sums the weights on the matrix pipe
-//     instead (a 0/1 matrix times P^T on 16x16x32).  o = O / d does not depend on m.
+//     fma + exp2 and half a bf16 pack; the denominator is summed on the
+//     matrix pipe (a 0/1 matrix times P^T on 16x16x32).  o = O / d does not
+//     depend on m.
 //   * Software pipeline: iteration j runs the QK^T MFMAs of tile j+1 next to
 //     the exponentials of tile j; with head_dim 64 also the P.V MFMAs of tile
 //     j-1 from operands held in registers, so that the matrix and vector
@@ -85,9 +85,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
   constexpr int KT = BN * D;             // elements of one K or V tile
   constexpr int DMA = BN * DC / kThreads;   // 16-byte DMA slots per thread per tile
   constexpr bool kDeferPV = D == 64;        // P.V one tile behind (registers permitting)
-  // Tile weight sums on the matrix pipe (a 0/1 matrix times P^T) where the
-  // contractions leave it room (head_dim 128), else on the vector ALU.
-  constexpr bool kSumOnMatrix = D == 128;
   // Separate arrays per buffer: the compiler then sees that the copies into
   // one buffer never alias the reads of the other, and does not make those
   // reads wait for the copies in flight.
@@ -269,7 +266,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
   auto weights = [&](f32x16_t (&s)[QB][KB], u32x4_t (&pf)[QB][NU], float (&ts)[QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float t0 = 0.f, t1 = 0.f;
       f32x4_t tm = {};
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
@@ -281,17 +277,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && QB == 1) ? 3 : 2) void prefil
         pf[qb][u][1] = pack_bf16x2(p[2], p[3]);
         pf[qb][u][2] = pack_bf16x2(p[4], p[5]);
         pf[qb][u][3] = pack_bf16x2(p[6], p[7]);
-        if constexpr (kSumOnMatrix) {
-          tm = mfma_16x16x32(ones16, pf[qb][u], tm);
-        } else {
-          t0 = add_bf16x2(pf[qb][u][0], t0);
-          t1 = add_bf16x2(pf[qb][u][1], t1);
-          t0 = add_bf16x2(pf[qb][u][2], t0);
-          t1 = add_bf16x2(pf[qb][u][3], t1);
-        }
+        tm = mfma_16x16x32(ones16, pf[qb][u], tm);
       }
-      if constexpr (kSumOnMatrix) ts[qb] = lhalf == 0 ? tm[0] : 0.f;
-      else ts[qb] = t0 + t1;
+      ts[qb] = lhalf == 0 ? tm[0] : 0.f;
     }
   };
 
