@@ -154,7 +154,7 @@ def chunked_prefill_measurement(dev, stream, reps: int):
     run = lambda: sa.sink_attn_prefill_chunked(q, k, v, sinks, cq, ck, inp["max_seqlen_q"],
                                                causal=True, scale=cfg.scale, out=out,
                                                stream=stream)
-    for _ in range(3):
+    for _ in range(10):
         run()
     torch.cuda.synchronize()
     e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -188,7 +188,7 @@ def kv_append_measurement(dev, stream, reps: int):
     vc = torch.zeros_like(kc)
     run = lambda: sa.sink_attn_kv_append(kn, vn, cu, pos, kc, vc, max_new=cfg["new"],
                                          stream=stream)
-    for _ in range(3):
+    for _ in range(10):
         run()
     torch.cuda.synchronize()
     e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -223,7 +223,7 @@ def multi_decode_measurement(dev, stream, reps: int):
     run = lambda: sa.sink_attn_decode_multi(q, kc, vc, lens, sinks, cfg.split_size, ns,
                                             scale=cfg.scale, out=out, partials=(po, pm, pd),
                                             stream=stream)
-    for _ in range(3):
+    for _ in range(10):
         run()
     torch.cuda.synchronize()
     e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -260,7 +260,7 @@ def fp8_decode_measurement(dev, stream, reps: int):
     run = lambda: sa.sink_attn_decode_fp8(q, kc, vc, ks, vs, lens, sinks, cfg.split_size, ns,
                                           scale=cfg.scale, out=out, partials=(po, pm, pd),
                                           stream=stream)
-    for _ in range(3):
+    for _ in range(10):
         run()
     torch.cuda.synchronize()
     e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -310,7 +310,7 @@ def paged_decode_measurement(dev, stream, reps: int, page_size: int = 16):
     run = lambda: sa.sink_attn_decode_paged(q, kp, vp, bt, lens, sinks, cfg.split_size, ns,
                                             scale=cfg.scale, out=out, partials=(po, pm, pd),
                                             stream=stream)
-    for _ in range(3):
+    for _ in range(10):
         run()
     torch.cuda.synchronize()
     e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -348,7 +348,7 @@ def hbm_read_reference(dev, stream, reps: int = 10):
     out = torch.zeros(blocks, dtype=torch.int32, device=dev)
     sp = stream.cuda_stream
     run = lambda: lib.hbm_read_probe(buf.data_ptr(), nbytes, blocks, out.data_ptr(), sp)
-    for _ in range(3):
+    for _ in range(10):
         if run() != 0:
             raise RuntimeError("hbm_read_probe failed")
     torch.cuda.synchronize()
@@ -381,7 +381,7 @@ def ragged_decode_measurement(dev, stream, batch: int, reps: int):
     run = lambda: sa.sink_attn_decode(q, kc, vc, lens, sinks, cfg.split_size, ns,
                                       scale=cfg.scale, out=out, partials=(po, pm, pd),
                                       stream=stream)
-    for _ in range(3):
+    for _ in range(10):
         run()
     torch.cuda.synchronize()
     e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
