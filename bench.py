@@ -530,7 +530,7 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(split_gbs / PEAK_HBM_GBS, 4),
-                                "traffic": traffic_d, "kernel": "decode_split_kernel<64,1,4,false>",
+                                "traffic": traffic_d, "kernel": "decode_split_kernel<64,1,4,false,false>",
                                 "algorithmic_bytes_per_launch": kv_bytes},
                    "frac_of_hbm_peak_incl_merge": round(dec_gbs / PEAK_HBM_GBS, 4)},
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
