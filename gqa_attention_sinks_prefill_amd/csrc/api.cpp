@@ -145,8 +145,12 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
                               const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
                               const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t head_dim, float scale, int32_t split_size, int32_t num_splits,
-                              float* part_o, float* part_m, float* part_d, void* stream) {
+                              float* part_o, float* part_m, float* part_d, void* stream,
+                              int32_t* counters = nullptr, void* o = nullptr, int64_t o_stride_b = 0,
+                              int64_t o_stride_tok = 0, int64_t o_stride_head = 0,
+                              float* lse = nullptr) {
   const bool fp8 = k_scale != nullptr || v_scale != nullptr;
+  const bool fused = counters != nullptr || o != nullptr;
   const bool paged = page_size != 0;
   const int64_t elem = fp8 ? 1 : 2;           // bytes per cached element
   if (batch < 0 || max_ctx < 0) return fail(SINK_ATTN_EINVAL, "batch and max_ctx must be >= 0");
@@ -176,6 +180,13 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
     return fail(SINK_ATTN_EINVAL, "a required pointer is null");
   if (paged && !aligned(block_tables, 4))
     return fail(SINK_ATTN_EINVAL, "block_tables must be 4-byte aligned");
+  if (fused) {
+    if (!counters || !o) return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+    if (!aligned(counters, 4) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
+      return fail(SINK_ATTN_EINVAL, "counters and lse must be 4-byte aligned, o 16-byte aligned");
+    if (!stride_ok(o_stride_b) || !stride_ok(o_stride_tok) || !stride_ok(o_stride_head))
+      return fail(SINK_ATTN_EINVAL, "output strides must be non-negative multiples of 8 elements");
+  }
   if (fp8 && (!k_scale || !v_scale || !aligned(k_scale, 4) || !aligned(v_scale, 4)))
     return fail(SINK_ATTN_EINVAL, "k_scale and v_scale must both be given, 4-byte aligned");
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
@@ -235,6 +246,21 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
   a.split_size = split_size;
   a.num_splits = num_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
+  if (fused) {
+    a.counters = counters;
+    a.merge.part_o = part_o;
+    a.merge.part_m = part_m;
+    a.merge.part_d = part_d;
+    a.merge.o = static_cast<uint16_t*>(o);
+    a.merge.o_sb = o_stride_b;
+    a.merge.o_st = o_stride_tok;
+    a.merge.o_sh = o_stride_head;
+    a.merge.lse = lse;
+    a.merge.rows = static_cast<int32_t>(static_cast<int64_t>(batch) * q_len * num_q_heads);
+    a.merge.q_len = q_len;
+    a.merge.num_q_heads = num_q_heads;
+    a.merge.num_splits = num_splits;
+  }
   return launched(sinkattn::launch_decode_split(a, head_dim, num_blocks, static_cast<hipStream_t>(stream)),
                   "decode_split");
 }
@@ -273,6 +299,27 @@ int sink_attn_decode_multi_split_fp8(const void* q, int64_t q_stride_b, int64_t 
                             0, seq_lens,
                             batch, max_ctx, sinks, num_q_heads, num_kv_heads, head_dim, scale,
                             split_size, num_splits, part_o, part_m, part_d, stream);
+}
+
+int sink_attn_decode_fused(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                           int64_t q_stride_head, int32_t q_len, const void* k_cache,
+                           const void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
+                           int64_t kv_stride_tok, const float* k_scale, const float* v_scale,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                           const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, float scale, int32_t split_size, int32_t num_splits,
+                           float* part_o, float* part_m, float* part_d, int32_t* counters,
+                           void* o, int64_t o_stride_b, int64_t o_stride_tok,
+                           int64_t o_stride_head, float* lse, void* stream) {
+  g_err[0] = '\0';
+  if ((k_scale == nullptr) != (v_scale == nullptr))
+    return fail(SINK_ATTN_EINVAL, "k_scale and v_scale must both be given or both be null");
+  if (batch > 0 && (!counters || !o)) return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  return decode_multi_split(q, q_stride_b, q_stride_tok, q_stride_head, q_len, k_cache, v_cache,
+                            kv_stride_b, kv_stride_head, kv_stride_tok, k_scale, v_scale, nullptr, 0,
+                            0, seq_lens, batch, max_ctx, sinks, num_q_heads, num_kv_heads,
+                            head_dim, scale, split_size, num_splits, part_o, part_m, part_d,
+                            stream, counters, o, o_stride_b, o_stride_tok, o_stride_head, lse);
 }
 
 int sink_attn_decode_paged_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
@@ -341,9 +388,11 @@ int sink_attn_merge_states(const float* part_o, const float* part_m, const float
   a.part_d = part_d;
   a.o = static_cast<uint16_t*>(o);
   a.o_sb = o_stride_b;
+  a.o_st = 0;
   a.o_sh = o_stride_head;
   a.lse = lse;
   a.rows = static_cast<int32_t>(rows);
+  a.q_len = 1;
   a.num_q_heads = num_q_heads;
   a.num_splits = num_splits;
   return launched(sinkattn::launch_merge(a, head_dim, static_cast<hipStream_t>(stream)), "merge_states");

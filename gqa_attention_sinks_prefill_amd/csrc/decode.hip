@@ -506,16 +506,6 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
   }
 }
 
-// One workgroup per unit.  head_dim 64 with up to 2 column blocks runs 2 waves
-// per SIMD (16 KB of LDS per wave); wider blocks and head_dim 128 need the
-// registers of 1 wave per SIMD.
-template <int D, int CB, int W, bool F8, bool PG>
-__global__ __launch_bounds__(64 * W, (D == 64 && CB <= 2) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[decode_lds0_elems<D, CB, W, F8>()];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[decode_lds1_elems<D, CB, W, F8>()];
-  decode_unit<D, CB, W, F8, PG>(a, blockIdx.x, v_lds0, v_lds1);
-}
-
 // Wave-wide reductions (64 lanes) for the merge.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -533,12 +523,10 @@ __device__ __forceinline__ float wave_sum(float x) {
 // kMergeRegs chunks' outputs; the weights are then broadcast lane to lane.
 constexpr int kMergeRegs = 16;
 
+// Merge of one (b, h) row's chunk states by one wave (lane = d).
 template <int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+__device__ __forceinline__ void merge_row(const MergeArgs& a, int row, int lane) {
   constexpr int DL = D / 64;                 // d values per lane
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
-  const int lane = threadIdx.x & 63;
   const int ns = a.num_splits;
   const float* pm = a.part_m + (int64_t)row * ns;
   const float* pd = a.part_d + (int64_t)row * ns;
@@ -586,14 +574,65 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  const int b = row / a.num_q_heads, h = row % a.num_q_heads;
-  uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh;
+  // row = (b * q_len + t) * num_q_heads + h
+  const int bt = row / a.num_q_heads, h = row % a.num_q_heads;
+  uint16_t* op = a.o + (int64_t)(bt / a.q_len) * a.o_sb + (int64_t)(bt % a.q_len) * a.o_st +
+                 (int64_t)h * a.o_sh;
 #pragma unroll
   for (int j = 0; j < DL; ++j) {
     const __bf16 v = (__bf16)(acc[j] * inv);
     op[lane + 64 * j] = __builtin_bit_cast(uint16_t, v);
   }
   if (a.lse != nullptr && lane == 0) a.lse[row] = W > 0.f ? M + __logf(W) : -INFINITY;
+}
+
+// Fused merge: after its chunk state is written, a workgroup counts itself in
+// for its (b, KV head, column slice); the one that arrives last -- every other
+// chunk's state is then written and, past the fences, visible -- merges the
+// slice's rows with the same per-row code as merge_kernel and resets the
+// counter for the next launch.
+template <int D, int CB, int W>
+__device__ __forceinline__ void decode_merge_if_last(const DecodeArgs& a, int unit) {
+  constexpr int NC = 16 * CB;
+  __shared__ int is_last;
+  const int hs = unit % a.head_slices;
+  unit /= a.head_slices;
+  const int g = unit % a.num_kv_heads;
+  unit /= a.num_kv_heads;
+  const int b = unit % a.batch;
+  int32_t* counter = a.counters + ((int64_t)b * a.num_kv_heads + g) * a.head_slices + hs;
+  __threadfence();                     // this thread's state stores, device-wide
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = atomicAdd(counter, 1) == a.num_splits - 1;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();                     // the other chunks' states, seen
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int x0 = hs * NC, nx = min(NC, a.ncols - x0);
+  for (int xl = wave; xl < nx; xl += W) {
+    const int x = x0 + xl;
+    merge_row<D>(a.merge, ((b * a.q_len + x / a.group) * a.num_q_heads) + g * a.group + x % a.group,
+                 lane);
+  }
+  if (threadIdx.x == 0) *counter = 0;
+}
+
+// One workgroup per unit.  head_dim 64 with up to 2 column blocks runs 2 waves
+// per SIMD (16 KB of LDS per wave); wider blocks and head_dim 128 need the
+// registers of 1 wave per SIMD.
+template <int D, int CB, int W, bool F8, bool PG>
+__global__ __launch_bounds__(64 * W, (D == 64 && CB <= 2) ? 2 : 1) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[decode_lds0_elems<D, CB, W, F8>()];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[decode_lds1_elems<D, CB, W, F8>()];
+  decode_unit<D, CB, W, F8, PG>(a, blockIdx.x, v_lds0, v_lds1);
+  if (a.counters != nullptr) decode_merge_if_last<D, CB, W>(a, blockIdx.x);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  merge_row<D>(a, row, threadIdx.x & 63);
 }
 
 }  // namespace

@@ -28,6 +28,19 @@ struct PrefillArgs {
   float scale_log2;       // softmax scale * log2(e)
 };
 
+struct MergeArgs {
+  const float* part_o;
+  const float* part_m;
+  const float* part_d;
+  uint16_t* o;
+  int64_t o_sb, o_st, o_sh;  // output strides: request, new token, head
+  float* lse;
+  int32_t rows;           // batch * q_len * num_q_heads
+  int32_t q_len;          // new tokens per request (1 for plain decode)
+  int32_t num_q_heads;
+  int32_t num_splits;
+};
+
 struct DecodeArgs {
   const uint16_t* q;
   int64_t q_sb, q_st, q_sh;  // request, new-token and head strides
@@ -55,19 +68,13 @@ struct DecodeArgs {
   int32_t split_size;
   int32_t num_splits;
   float scale_log2;
+  // Fused merge (else null): one arrival counter per (b, KV head, column
+  // slice), zero before the launch and left zero after it; the workgroup that
+  // completes a slice's last chunk merges its rows into merge.o / merge.lse.
+  int32_t* counters;
+  MergeArgs merge;
 };
 
-struct MergeArgs {
-  const float* part_o;
-  const float* part_m;
-  const float* part_d;
-  uint16_t* o;
-  int64_t o_sb, o_sh;
-  float* lse;
-  int32_t rows;           // batch * num_q_heads
-  int32_t num_q_heads;
-  int32_t num_splits;
-};
 
 struct KvAppendArgs {
   const uint16_t* k_new;

@@ -238,6 +238,35 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride
                         int32_t head_dim, void* stream);
 
 /*
+ * Split decode and merge in one launch: the work of
+ * sink_attn_decode_multi_split (bf16 caches, or FP8 E4M3 caches when k_scale
+ * and v_scale are given -- both or neither) followed by
+ * sink_attn_merge_states, with the merge done by whichever workgroup
+ * finishes the last chunk of a (request, KV head, column slice): it counts
+ * itself in on `counters`, and the last arrival merges that slice's rows.
+ * Same results as the two calls (the merge is the same code).
+ *   part_o, part_m, part_d: as sink_attn_decode_multi_split (still written).
+ *   counters: int32, device, at least batch * num_kv_heads *
+ *       ceil(q_len * (num_q_heads / num_kv_heads) / 16) elements, all zero
+ *       before the first call; every call leaves them zero.  Calls that run
+ *       concurrently must not share counters.
+ *   o [B, q_len, Hq, D] bf16: new token t of request b, head h at
+ *       o + b*o_stride_b + t*o_stride_tok + h*o_stride_head (d unit-stride).
+ *   lse: NULL, or fp32 [B, q_len, Hq] contiguous.
+ *   Other arguments and errors as sink_attn_decode_multi_split.
+ */
+int sink_attn_decode_fused(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                           int64_t q_stride_head, int32_t q_len, const void* k_cache,
+                           const void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
+                           int64_t kv_stride_tok, const float* k_scale, const float* v_scale,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                           const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, float scale, int32_t split_size, int32_t num_splits,
+                           float* part_o, float* part_m, float* part_d, int32_t* counters,
+                           void* o, int64_t o_stride_b, int64_t o_stride_tok,
+                           int64_t o_stride_head, float* lse, void* stream);
+
+/*
  * FP8 KV cache.  The pages speak of FP8 only for weights; decode, though, is
  * bound by the bytes of the cache it streams ("Hosting Qwen on Blackwell",
  * section "Decoders"), and one byte per element halves them.  Format: OCP FP8

@@ -852,11 +852,120 @@ def test_kv_append_paged_bitwise(fp8, P, D):
     assert torch.equal(view(kg.cpu()), view(ko)) and torch.equal(view(vg.cpu()), view(vo))
 
 
+# ---------------------------------------------------- one-launch decode --
+def _fused_gpu(inp, split, *, fp8=False, counters=None):
+    q = _q4(inp["q"]).to(DEV)
+    kc, vc = inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    B, q_len, Hq, D = q.shape
+    ns = -(-kc.shape[2] // split)
+    po = torch.full((B, q_len, Hq, ns, D), float("nan"), device=DEV)
+    pm = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    pd = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    out = torch.full((B, q_len, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, q_len, Hq), float("nan"), device=DEV)
+    if counters is None:
+        counters = sa.decode_counters(B, Hq, kc.shape[1], q_len, DEV)
+    kw = dict(k_scale=inp["k_scale"].to(DEV), v_scale=inp["v_scale"].to(DEV)) if fp8 else {}
+    sa.sink_attn_decode_fused(q, kc, vc, inp["seq_lens"].to(DEV), inp["sinks"].to(DEV), split,
+                              ns, counters=counters, out=out, lse=lse, partials=(po, pm, pd),
+                              **kw)
+    torch.cuda.synchronize()
+    return out, lse, counters
+
+
+def _split_merge_gpu(inp, split, fp8):
+    if fp8:
+        out, lse, _ = _fp8_gpu(inp, split)
+        return out, lse
+    return _decode_multi_gpu(dict(inp, q=_q4(inp["q"])), split)
+
+
+def _bitwise(a, b):
+    return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# (lens, q_len, Hq, Hkv, D, split): the waves each chunk gets (1, 2 or 4) and
+# the column blocks per workgroup follow from the shape, so these cover all of
+# them -- head_dim 64 with one 16-column block (4 waves), head_dim 128 with
+# 1024 chunks (1 wave) and 512 chunks (2 waves), few chunks (4 waves), two
+# column blocks at 1024 chunks, and 128 columns per KV head (two slices).
+_FUSED_CASES = [
+    ([0, 1, 65, 257, 1000, 3000], 1, 64, 8, 64, 256),
+    ([5, 700, 8192, 8192], 1, 64, 8, 128, 256),
+    ([5, 700, 4096, 4096], 1, 64, 8, 128, 256),
+    ([3, 64, 1000], 2, 64, 4, 128, 256),
+    ([4, 129, 8192, 8000], 4, 64, 8, 64, 256),
+    ([16, 130, 700], 16, 64, 8, 64, 512),
+]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("case", range(len(_FUSED_CASES)))
+def test_decode_fused_is_bitwise_split_then_merge(case, fp8):
+    """The one-launch call gives bitwise the output and lse of the two-call
+    path (the merge is the same per-row code), and leaves its counters zero."""
+    lens, q_len, Hq, Hkv, D, split = _FUSED_CASES[case]
+    mk = _fp8_cfg if fp8 else _multi_cfg
+    inp = mk(lens, q_len, Hq, Hkv, D, seed=190 + case, split=split,
+             edges={0: float("-inf"), Hq - 1: 20.0})
+    out_f, lse_f, cnt = _fused_gpu(inp, split, fp8=fp8)
+    out_s, lse_s = _split_merge_gpu(inp, split, fp8)
+    assert _bitwise(out_f, out_s), f"fused output differs from split+merge, case {case}"
+    assert torch.equal(lse_f, lse_s), f"fused lse differs from split+merge, case {case}"
+    assert int(cnt.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_fused_all_rows_against_the_oracle(fp8):
+    """Ragged lengths (0, shorter than q_len, chunk edges) on every row."""
+    lens, q_len, Hq, Hkv, D = [0, 2, 3, 64, 257, 513, 1000], 3, 32, 4, 64
+    mk = _fp8_cfg if fp8 else _multi_cfg
+    inp = mk(lens, q_len, Hq, Hkv, D, seed=200, split=256, edges={1: float("-inf"), 5: 20.0})
+    out, lse, _ = _fused_gpu(inp, 256, fp8=fp8)
+    if fp8:
+        o_ref, lse_ref, _ = _fp8_ref(inp)
+    else:
+        o_ref, lse_ref, _ = oracle.decode_multi(inp["q"], inp["k_cache"], inp["v_cache"],
+                                                inp["seq_lens"], inp["sinks"])
+    assert_close(out.reshape(-1, D), o_ref, what=f"fused decode fp8={fp8}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what=f"fused decode lse fp8={fp8}")
+
+
+def test_decode_fused_reuses_its_counters_across_shapes():
+    """One counter buffer serves calls of different shapes back to back (the
+    last arrival of every slice resets its counter)."""
+    big = _multi_cfg([7, 3000, 2048, 90], 4, 64, 8, 64, seed=210, split=256)
+    small = _multi_cfg([1, 500], 1, 64, 8, 64, seed=211, split=256)
+    cnt = sa.decode_counters(4, 64, 8, 4, DEV)
+    for inp in (big, small, big):
+        out_f, lse_f, _ = _fused_gpu(inp, 256, counters=cnt)
+        out_s, lse_s = _split_merge_gpu(inp, 256, False)
+        assert _bitwise(out_f, out_s) and torch.equal(lse_f, lse_s)
+        assert int(cnt.abs().sum()) == 0
+
+
+def test_decode_fused_strided_output():
+    """Output rows inside a wider buffer: only the addressed elements change."""
+    inp = _multi_cfg([50, 600], 2, 16, 2, 128, seed=220, split=256)
+    q = inp["q"].to(DEV)
+    big = torch.full((2, 3, 16, 144), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = big[:, 1:, :, 8:136]
+    sa.sink_attn_decode_fused(q, inp["k_cache"].to(DEV), inp["v_cache"].to(DEV),
+                              inp["seq_lens"].to(DEV), inp["sinks"].to(DEV), 256, out=out)
+    torch.cuda.synchronize()
+    ref, _ = _split_merge_gpu(inp, 256, False)
+    assert _bitwise(out.contiguous(), ref)
+    rest = big.clone()
+    rest[:, 1:, :, 8:136] = 0
+    assert torch.isnan(rest[:, :1].float()).all() and torch.isnan(rest[..., :8].float()).all()
+    assert torch.isnan(rest[..., 136:].float()).all()
+
+
 # ----------------------------------------------------------- graph capture --
 def test_decode_and_prefill_replay_from_a_captured_graph():
     """The calls only enqueue kernels on the caller's stream (no allocation,
     no synchronisation, no memset), so they can be captured in a HIP graph.
-    Capture prefill + split decode + merge once, then replay with new inputs
+    Capture prefill + split decode + merge + one-launch decode once, then replay with new inputs
     copied into the captured buffers, eager work and a synchronisation between
     replays, and check every replay against an eager run."""
     g = torch.Generator().manual_seed(170)
@@ -874,10 +983,15 @@ def test_decode_and_prefill_replay_from_a_captured_graph():
     pm = torch.empty(4, 16, ns, device=DEV)
     pd = torch.empty(4, 16, ns, device=DEV)
     o_d = torch.empty(4, 16, 64, dtype=torch.bfloat16, device=DEV)
+    o_f = torch.empty_like(o_d)
+    cnt = sa.decode_counters(4, 16, 2, 1, DEV)
+    fpart = (torch.empty_like(po), torch.empty_like(pm), torch.empty_like(pd))
 
     def step():
         sa.sink_attn_prefill(q_p, k_p, v_p, s_p, cu, pre["max_seqlen"], out=o_p)
         sa.sink_attn_decode(q_d, kc, vc, lens, s_d, 512, ns, out=o_d, partials=(po, pm, pd))
+        sa.sink_attn_decode_fused(q_d, kc, vc, lens, s_d, 512, ns, counters=cnt, out=o_f,
+                                  partials=fpart)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -894,12 +1008,14 @@ def test_decode_and_prefill_replay_from_a_captured_graph():
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        got_p, got_d = o_p.clone(), o_d.clone()
+        got_p, got_d, got_f = o_p.clone(), o_d.clone(), o_f.clone()
         scratch = torch.randn(1 << 20, device=DEV).sum()   # eager work between replays
         step()                                   # eager reference on the same inputs
         torch.cuda.synchronize()
         assert torch.equal(got_p.view(torch.int16), o_p.view(torch.int16)), f"prefill replay {rep}"
         assert torch.equal(got_d.view(torch.int16), o_d.view(torch.int16)), f"decode replay {rep}"
+        assert torch.equal(got_f.view(torch.int16), o_d.view(torch.int16)), f"fused replay {rep}"
+        assert int(cnt.abs().sum()) == 0
         assert torch.isfinite(scratch)
     # and the replayed decode is right, not merely repeatable
     o_ref, _, _ = oracle.decode(q_d.cpu(), dec["k_cache"], dec["v_cache"], dec["seq_lens"],
