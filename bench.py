@@ -24,9 +24,10 @@ After the timed steps (not part of them): `hbm_read_reference` times a plain
 streaming-read kernel (libhbmprobe.so) and `decode.frac_of_measured_read`
 relates the decode to it; `extra` holds the other workloads' lines -- the
 head_dim 128 varlen prefill, chunked prefill, multi-token decode, decode over
-FP8 caches and over 16-token pages, KV-cache append and the ragged
-long-context decode at B = 1, 8,
-32, 128 (B < 32 is launch / latency bound and flagged so).
+FP8 caches and over 16-token pages, KV-cache append, the ragged
+long-context decode at B = 1, 8, 32, 128 (B < 32 is latency bound and
+flagged so) and the one-launch decode (sink_attn_decode_fused) beside split +
+merge; the ragged and one-launch lines take device time from HIP-graph replay.
 """
 from __future__ import annotations
 
@@ -365,41 +366,99 @@ def hbm_read_reference(dev, stream, reps: int = 10):
             "bytes": nbytes, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s"}
 
 
-def ragged_decode_measurement(dev, stream, batch: int, reps: int):
-    """KV GB/s of split decode + merge over contexts U[1024, 32768] (64 / 8 heads,
-    d 64, 1024-token chunks); B = 1 and 8 are launch / latency bound."""
-    cfg = wl.ragged_decode(batch)
+def graph_ms(run, stream, calls: int = 20, reps: int = 10) -> float:
+    """Mean device time of one call: `calls` calls captured in one HIP graph,
+    replayed `reps` times between HIP events on `stream` (no host launch
+    overhead inside the timed region -- what a serving loop that replays a
+    captured step sees).  `run(s)` enqueues one call on stream s."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _ in range(10):
+            run(side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        for _ in range(calls):
+            run(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()
+        torch.cuda.synchronize()
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(reps)]
+        for a, b in e:
+            a.record(stream)
+            graph.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+    del graph
+    return float(np.mean([a.elapsed_time(b) for a, b in e])) / calls
+
+
+def _decode_buffers(cfg, dev):
     d = wl.decode_inputs(cfg)
     q, kc, vc = d["q"].to(dev), d["k_cache"].to(dev), d["v_cache"].to(dev)
-    lens, sinks = d["seq_lens"].to(dev), d["sinks"].to(dev)
     B, Hq, D = q.shape
     ns = cfg.num_splits
-    po = torch.empty(B, Hq, ns, D, device=dev)
-    pm = torch.empty(B, Hq, ns, device=dev)
-    pd = torch.empty(B, Hq, ns, device=dev)
-    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
-    run = lambda: sa.sink_attn_decode(q, kc, vc, lens, sinks, cfg.split_size, ns,
-                                      scale=cfg.scale, out=out, partials=(po, pm, pd),
-                                      stream=stream)
-    for _ in range(10):
-        run()
-    torch.cuda.synchronize()
-    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-         for _ in range(reps)]
-    for a, b in e:
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
-    kv = wl.decode_kv_bytes(d["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
-    gbs = kv / (ms * 1e-3) / 1e9
-    del kc, vc
+    bufs = dict(q=q, kc=kc, vc=vc, lens=d["seq_lens"].to(dev), sinks=d["sinks"].to(dev), ns=ns,
+                part=(torch.empty(B, Hq, ns, D, device=dev), torch.empty(B, Hq, ns, device=dev),
+                      torch.empty(B, Hq, ns, device=dev)),
+                out=torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev),
+                counters=sa.decode_counters(B, Hq, kc.shape[1], 1, dev),
+                kv=wl.decode_kv_bytes(d["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim))
+    return bufs
+
+
+def _split_merge(cfg, x):
+    return lambda s: sa.sink_attn_decode(x["q"], x["kc"], x["vc"], x["lens"], x["sinks"],
+                                         cfg.split_size, x["ns"], scale=cfg.scale, out=x["out"],
+                                         partials=x["part"], stream=s)
+
+
+def _one_launch(cfg, x):
+    return lambda s: sa.sink_attn_decode_fused(x["q"], x["kc"], x["vc"], x["lens"], x["sinks"],
+                                               cfg.split_size, x["ns"], scale=cfg.scale,
+                                               counters=x["counters"], out=x["out"],
+                                               partials=x["part"], stream=s)
+
+
+def ragged_decode_measurement(dev, stream, batch: int, reps: int):
+    """KV GB/s of split decode + merge over contexts U[1024, 32768] (64 / 8 heads,
+    d 64, 1024-token chunks), device time from graph replay; B = 1 and 8 are
+    latency bound."""
+    cfg = wl.ragged_decode(batch)
+    x = _decode_buffers(cfg, dev)
+    ms = graph_ms(_split_merge(cfg, x), stream, reps=max(3, reps // 2))
+    gbs = x["kv"] / (ms * 1e-3) / 1e9
+    kv = x["kv"]
+    del x
     torch.cuda.empty_cache()
     return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
-            "metric": "decode KV GB/s (split + merge)", "mean_ms": round(ms, 4),
+            "metric": "decode KV GB/s (split + merge, graph replay)", "mean_ms": round(ms, 4),
             "algorithmic_bytes_per_step": kv,
             "latency_bound": batch < 32,
+            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
+def one_launch_decode_measurement(dev, stream, cfg, reps: int):
+    """sink_attn_decode_fused (split decode whose last workgroup per slice
+    merges) against split + merge, both from graph replay in the same run."""
+    x = _decode_buffers(cfg, dev)
+    reps = max(3, reps // 2)
+    two = graph_ms(_split_merge(cfg, x), stream, reps=reps)
+    one = graph_ms(_one_launch(cfg, x), stream, reps=reps)
+    two = min(two, graph_ms(_split_merge(cfg, x), stream, reps=reps))
+    one = min(one, graph_ms(_one_launch(cfg, x), stream, reps=reps))
+    gbs = x["kv"] / (one * 1e-3) / 1e9
+    kv = x["kv"]
+    del x
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
+            "metric": "decode KV GB/s, one launch (graph replay)", "mean_ms": round(one, 4),
+            "split_merge_ms_same_run": round(two, 4), "algorithmic_bytes_per_step": kv,
             "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
@@ -545,6 +604,8 @@ def main():
                         kv_append_measurement(dev, stream, max(3, args.steps // 2))]
         res["extra"] += [ragged_decode_measurement(dev, stream, b, max(3, args.steps // 4))
                          for b in wl.RAGGED_BATCHES]
+        res["extra"] += [one_launch_decode_measurement(dev, stream, c, max(3, args.steps // 4))
+                         for c in (wl.SPLIT_DECODE, wl.ragged_decode(1), wl.ragged_decode(128))]
     if run_d and not args.no_extra:
         ref = hbm_read_reference(dev, stream)
         res["hbm_read_reference"] = ref

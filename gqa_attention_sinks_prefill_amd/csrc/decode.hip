@@ -95,6 +95,17 @@ constexpr int decode_lds1_elems() {
   return cmax(W * v_tile_elems<D, F8>(), W == 1 && CB > 2 ? 2 * (CB - 2) * 16 * D : 0);
 }
 
+// Chunk states that another workgroup merges in the same launch cross L2
+// caches (one per XCD): they are written and read with device-scope accesses
+// (sc1), which are coherent across the XCDs without a cache-wide writeback
+// or invalidate.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One work unit: chunk c of request b, KV head g, column slice hs, on W waves.
 // F8: the caches hold FP8 E4M3 codes with a dequantization scale per KV head;
 // the codes convert exactly to bf16 for the MFMAs, k_scale joins the softmax
@@ -145,17 +156,28 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
     return (((int64_t)b * a.q_len + x / a.group) * a.num_q_heads + g * a.group + x % a.group) *
                a.num_splits + c;
   };
+  // state stores: device scope when a workgroup of this launch merges them
+  const bool dev_scope = a.counters != nullptr;
+  auto put = [&](float* p, float v) {
+    if (dev_scope) store_dev(p, v); else *p = v;
+  };
+  auto put_nt = [&](float* p, float v) {
+    if (dev_scope) store_dev(p, v); else store_nt(p, v);
+  };
 
   // A chunk past the request's end without the sink (ragged batches have many)
   // has the state (o, m, d) = (0, -inf, 0): write it and leave.
+  // (In one launch the merge stops at the request's last chunk with keys, so
+  // there such chunks write nothing.)
   if (n == 0 && c != 0) {
+    if (dev_scope) return;
     for (int item = tid; item < nx * D; item += kBlock) {
       const int64_t row = out_row(x0 + item / D);
       const int d = item % D;
-      a.part_o[row * D + d] = 0.f;
+      put(a.part_o + row * D + d, 0.f);
       if (d == 0) {
-        a.part_m[row] = -INFINITY;
-        a.part_d[row] = 0.f;
+        put(a.part_m + row, -INFINITY);
+        put(a.part_d + row, 0.f);
       }
     }
     return;
@@ -441,8 +463,8 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
         *reinterpret_cast<f32x4_t*>(stg + col * D + 4 * ((4 * db + lgrp) ^ col)) = acc[cb][db] * inv;
       if (lgrp == 0 && cb * 16 + col < nx) {
         const int64_t row = out_row(x0 + cb * 16 + col);
-        store_nt(a.part_m + row, lt > 0.f ? m[cb] * kLn2 : -INFINITY);
-        store_nt(a.part_d + row, lt);
+        put_nt(a.part_m + row, lt > 0.f ? m[cb] * kLn2 : -INFINITY);
+        put_nt(a.part_d + row, lt);
       }
     }
     __syncthreads();
@@ -453,7 +475,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
       const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + xc * D + 4 * (d4 ^ xc));
       float* op = a.part_o + out_row(x0 + xl) * D + 4 * d4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store_nt(op + i, v[i]);
+      for (int i = 0; i < 4; ++i) put_nt(op + i, v[i]);
     }
   } else {
     // ---- merge the W waves' states through LDS ------------------------------
@@ -497,10 +519,10 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
       const float inv = wsum > 0.f ? out_scale / wsum : 0.f;
       float* op = a.part_o + row * D + 4 * c4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) op[i] = o[i] * inv;
+      for (int i = 0; i < 4; ++i) put(op + i, o[i] * inv);
       if (c4 == 0) {
-        a.part_m[row] = wsum > 0.f ? M * kLn2 : -INFINITY;
-        a.part_d[row] = wsum;
+        put(a.part_m + row, wsum > 0.f ? M * kLn2 : -INFINITY);
+        put(a.part_d + row, wsum);
       }
     }
   }
@@ -523,33 +545,59 @@ __device__ __forceinline__ float wave_sum(float x) {
 // kMergeRegs chunks' outputs; the weights are then broadcast lane to lane.
 constexpr int kMergeRegs = 16;
 
-// Merge of one (b, h) row's chunk states by one wave (lane = d).
+// Merge of one (b, h) row's first ns chunk states by one wave (lane = d), in
+// two steps: merge_load issues the loads of the first kMergeRegs chunks' o
+// and the first 64 chunks' m and d (one round trip), merge_finish combines
+// them (and reads any further chunks itself).  DEV: device-scope loads
+// (states written by this launch).
 template <int D>
-__device__ __forceinline__ void merge_row(const MergeArgs& a, int row, int lane) {
-  constexpr int DL = D / 64;                 // d values per lane
-  const int ns = a.num_splits;
-  const float* pm = a.part_m + (int64_t)row * ns;
-  const float* pd = a.part_d + (int64_t)row * ns;
-  const float* po = a.part_o + (int64_t)row * ns * D;
+struct MergeIn {
+  float ov[kMergeRegs][D / 64];
+  float m0, d0;
+};
 
-  float ov[kMergeRegs][DL];
+template <int D, bool DEV>
+__device__ __forceinline__ float merge_ld(const float* p) {
+  return DEV ? load_dev(p) : *p;
+}
+
+template <int D, bool DEV>
+__device__ __forceinline__ void merge_load(const MergeArgs& a, int row, int lane, int ns,
+                                           MergeIn<D>& in) {
+  constexpr int DL = D / 64;                 // d values per lane
+  const int64_t first = (int64_t)row * a.num_splits;
+  const float* po = a.part_o + first * D;
 #pragma unroll
   for (int c = 0; c < kMergeRegs; ++c)
 #pragma unroll
-    for (int j = 0; j < DL; ++j) ov[c][j] = c < ns ? po[c * D + lane + 64 * j] : 0.f;
+    for (int j = 0; j < DL; ++j)
+      in.ov[c][j] = c < ns ? merge_ld<D, DEV>(po + c * D + lane + 64 * j) : 0.f;
+  in.m0 = lane < ns ? merge_ld<D, DEV>(a.part_m + first + lane) : -INFINITY;
+  in.d0 = lane < ns ? merge_ld<D, DEV>(a.part_d + first + lane) : 0.f;
+}
 
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < ns; c0 += 64) {
+template <int D, bool DEV>
+__device__ __forceinline__ void merge_finish(const MergeArgs& a, int row, int lane, int ns,
+                                             const MergeIn<D>& in) {
+  auto ld = [](const float* p) { return merge_ld<D, DEV>(p); };
+  constexpr int DL = D / 64;
+  const int64_t first = (int64_t)row * a.num_splits;
+  const float* pm = a.part_m + first;
+  const float* pd = a.part_d + first;
+  const float* po = a.part_o + first * D;
+  float M = fmaxf(-INFINITY, wave_max(in.m0));
+  for (int c0 = 64; c0 < ns; c0 += 64) {
     const int c = c0 + lane;
-    M = fmaxf(M, wave_max(c < ns ? pm[c] : -INFINITY));
+    M = fmaxf(M, wave_max(c < ns ? ld(pm + c) : -INFINITY));
   }
   float W = 0.f;
   float acc[DL] = {};
   if (M != -INFINITY) {
     for (int c0 = 0; c0 < ns; c0 += 64) {
       const int c = c0 + lane;
-      const float mc = c < ns ? pm[c] : -INFINITY;
-      const float w = mc == -INFINITY ? 0.f : pd[c] * fast_exp2((mc - M) * kLog2e);
+      const float mc = c0 == 0 ? in.m0 : (c < ns ? ld(pm + c) : -INFINITY);
+      const float dc = c0 == 0 ? in.d0 : (c < ns ? ld(pd + c) : 0.f);
+      const float w = mc == -INFINITY ? 0.f : dc * fast_exp2((mc - M) * kLog2e);
       W += wave_sum(w);
       const int cn = min(64, ns - c0);
       auto wt = [&](int k) {
@@ -562,14 +610,14 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int row, int lane)
           if (r < cn) {
             const float wk = wt(r);
 #pragma unroll
-            for (int j = 0; j < DL; ++j) acc[j] += wk * ov[r][j];
+            for (int j = 0; j < DL; ++j) acc[j] += wk * in.ov[r][j];
           }
         k = kMergeRegs;
       }
       for (; k < cn; ++k) {
         const float wk = wt(k);
 #pragma unroll
-        for (int j = 0; j < DL; ++j) acc[j] += wk * po[(int64_t)(c0 + k) * D + lane + 64 * j];
+        for (int j = 0; j < DL; ++j) acc[j] += wk * ld(po + (int64_t)(c0 + k) * D + lane + 64 * j);
       }
     }
   }
@@ -586,11 +634,16 @@ __device__ __forceinline__ void merge_row(const MergeArgs& a, int row, int lane)
   if (a.lse != nullptr && lane == 0) a.lse[row] = W > 0.f ? M + __logf(W) : -INFINITY;
 }
 
-// Fused merge: after its chunk state is written, a workgroup counts itself in
-// for its (b, KV head, column slice); the one that arrives last -- every other
-// chunk's state is then written and, past the fences, visible -- merges the
-// slice's rows with the same per-row code as merge_kernel and resets the
-// counter for the next launch.
+// Fused merge: once its chunk state is written (device-scope stores, all
+// acknowledged), a workgroup counts itself in for its (b, KV head, column
+// slice); the one that arrives last -- every other chunk's state is then
+// complete -- reads them with device-scope loads, merges the slice's rows with
+// the same per-row code as merge_kernel and resets the counter for the next
+// launch.  Only chunk 0 and the chunks holding keys take part: the others'
+// state (0, -inf, 0) adds nothing to a merge.
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 template <int D, int CB, int W>
 __device__ __forceinline__ void decode_merge_if_last(const DecodeArgs& a, int unit) {
   constexpr int NC = 16 * CB;
@@ -600,21 +653,28 @@ __device__ __forceinline__ void decode_merge_if_last(const DecodeArgs& a, int un
   const int g = unit % a.num_kv_heads;
   unit /= a.num_kv_heads;
   const int b = unit % a.batch;
+  const int c = unit / a.batch;
+  const int len = a.seq_lens[b];
+  const int live = (int)max((int64_t)1, min((int64_t)a.num_splits,
+                                              ((int64_t)len + a.split_size - 1) / a.split_size));
+  if (c >= live) return;
   int32_t* counter = a.counters + ((int64_t)b * a.num_kv_heads + g) * a.head_slices + hs;
-  __threadfence();                     // this thread's state stores, device-wide
   __syncthreads();
-  if (threadIdx.x == 0) is_last = atomicAdd(counter, 1) == a.num_splits - 1;
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // every wave's state stores acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = atomicAdd(counter, 1) == live - 1;
   __syncthreads();
   if (!is_last) return;
-  __threadfence();                     // the other chunks' states, seen
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int x0 = hs * NC, nx = min(NC, a.ncols - x0);
   for (int xl = wave; xl < nx; xl += W) {
     const int x = x0 + xl;
-    merge_row<D>(a.merge, ((b * a.q_len + x / a.group) * a.num_q_heads) + g * a.group + x % a.group,
-                 lane);
+    const int row = ((b * a.q_len + x / a.group) * a.num_q_heads) + g * a.group + x % a.group;
+    MergeIn<D> in;
+    merge_load<D, true>(a.merge, row, lane, live, in);
+    merge_finish<D, true>(a.merge, row, lane, live, in);
   }
-  if (threadIdx.x == 0) *counter = 0;
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One workgroup per unit.  head_dim 64 with up to 2 column blocks runs 2 waves
@@ -632,7 +692,9 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
-  merge_row<D>(a, row, threadIdx.x & 63);
+  MergeIn<D> in;
+  merge_load<D, false>(a, row, threadIdx.x & 63, a.num_splits, in);
+  merge_finish<D, false>(a, row, threadIdx.x & 63, a.num_splits, in);
 }
 
 }  // namespace

@@ -244,8 +244,11 @@ int sink_attn_kv_append(const void* k_new, const void* v_new, int64_t new_stride
  * sink_attn_merge_states, with the merge done by whichever workgroup
  * finishes the last chunk of a (request, KV head, column slice): it counts
  * itself in on `counters`, and the last arrival merges that slice's rows.
- * Same results as the two calls (the merge is the same code).
- *   part_o, part_m, part_d: as sink_attn_decode_multi_split (still written).
+ * Same results as the two calls (the merge is the same code; chunks past a
+ * request's end hold (0, -inf, 0) and add nothing, so they are left out).
+ *   part_o, part_m, part_d: as sink_attn_decode_multi_split, except that the
+ *       states of chunks past a request's end (chunk c > 0 with
+ *       c * split_size >= seq_lens[b]) are not written.
  *   counters: int32, device, at least batch * num_kv_heads *
  *       ceil(q_len * (num_q_heads / num_kv_heads) / 16) elements, all zero
  *       before the first call; every call leaves them zero.  Calls that run
