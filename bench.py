@@ -27,7 +27,10 @@ head_dim 128 varlen prefill, chunked prefill, multi-token decode, decode over
 FP8 caches and over 16-token pages, KV-cache append, the ragged
 long-context decode at B = 1, 8, 32, 128 (B < 32 is latency bound and
 flagged so) and the one-launch decode (sink_attn_decode_fused) beside split +
-merge; the ragged and one-launch lines take device time from HIP-graph replay.
+merge; the ragged, one-launch and append lines take device time from HIP-graph
+replay and cycle through copies of their inputs so that each call reads from
+HBM rather than from the 256 MiB Infinity Cache (every other line streams at
+least 512 MiB per call).
 """
 from __future__ import annotations
 
@@ -177,34 +180,34 @@ def chunked_prefill_measurement(dev, stream, reps: int):
 
 def kv_append_measurement(dev, stream, reps: int):
     """GB/s (bytes read + written) of appending 1024 new tokens to each of 64
-    requests' HND caches (8 KV heads, d 64, 8192 slots), token-major rows in."""
+    requests' HND caches (8 KV heads, d 64, 8192 slots), token-major rows in;
+    device time from graph replay, cycling through copies of the new rows and
+    of the caches (one call moves 256 MiB)."""
     cfg = wl.KV_APPEND
     counts = [cfg["new"]] * cfg["batch"]
     inp = wl.kv_append_inputs(counts, cfg["max_ctx"], cfg["num_kv_heads"], cfg["head_dim"],
                               cfg["seed"])
+    moved = 2.0 * 2 * sum(counts) * cfg["num_kv_heads"] * cfg["head_dim"] * 2   # K+V, read + write
+    n = rotation(moved)
     kn, vn = inp["k_new"].to(dev), inp["v_new"].to(dev)
     cu, pos = inp["cu_seqlens_new"].to(dev), inp["cache_pos"].to(dev)
     shape = (cfg["batch"], cfg["num_kv_heads"], cfg["max_ctx"], cfg["head_dim"])
-    kc = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
-    vc = torch.zeros_like(kc)
-    run = lambda: sa.sink_attn_kv_append(kn, vn, cu, pos, kc, vc, max_new=cfg["new"],
-                                         stream=stream)
-    for _ in range(10):
-        run()
-    torch.cuda.synchronize()
-    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-         for _ in range(reps)]
-    for a, b in e:
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
-    moved = 2.0 * 2 * sum(counts) * cfg["num_kv_heads"] * cfg["head_dim"] * 2   # K+V, read + write
+    sets = [(kn, vn, torch.zeros(shape, dtype=torch.bfloat16, device=dev),
+             torch.zeros(shape, dtype=torch.bfloat16, device=dev))]
+    sets += [(kn.clone(), vn.clone(), torch.zeros_like(sets[0][2]), torch.zeros_like(sets[0][3]))
+             for _ in range(n - 1)]
+
+    def run(s, i):
+        a, b, kc, vc = sets[i % n]
+        sa.sink_attn_kv_append(a, b, cu, pos, kc, vc, max_new=cfg["new"], stream=s)
+
+    ms = graph_ms(run, stream, reps=max(3, reps // 2))
     gbs = moved / (ms * 1e-3) / 1e9
+    del sets
+    torch.cuda.empty_cache()
     return {"workload": cfg["name"], "value": round(gbs, 1), "unit": "GB/s",
-            "metric": "KV-cache append GB/s (bytes read + written)", "mean_ms": round(ms, 4),
-            "algorithmic_bytes": moved,
+            "metric": "KV-cache append GB/s (bytes read + written, graph replay)",
+            "mean_ms": round(ms, 4), "algorithmic_bytes": moved, "copies_rotated": n,
             "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
@@ -366,23 +369,30 @@ def hbm_read_reference(dev, stream, reps: int = 10):
             "bytes": nbytes, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s"}
 
 
+def rotation(touched_bytes: float) -> int:
+    """Copies of a call's inputs to cycle through so that one round of them
+    touches >= 1 GiB: a timed call then finds its bytes in HBM, not left in
+    the 256 MiB Infinity Cache by the call before."""
+    return int(min(32, max(1, -(-(1 << 30) // max(int(touched_bytes), 1)))))
+
+
 def graph_ms(run, stream, calls: int = 20, reps: int = 10) -> float:
     """Mean device time of one call: `calls` calls captured in one HIP graph,
     replayed `reps` times between HIP events on `stream` (no host launch
     overhead inside the timed region -- what a serving loop that replays a
-    captured step sees).  `run(s)` enqueues one call on stream s."""
+    captured step sees).  `run(s, i)` enqueues call i on stream s."""
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     with torch.cuda.stream(side):
-        for _ in range(10):
-            run(side)
+        for i in range(10):
+            run(side, i)
     stream.wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         cap = torch.cuda.current_stream()
-        for _ in range(calls):
-            run(cap)
+        for i in range(calls):
+            run(cap, i)
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         graph.replay()
@@ -399,30 +409,37 @@ def graph_ms(run, stream, calls: int = 20, reps: int = 10) -> float:
 
 
 def _decode_buffers(cfg, dev):
+    """Inputs of a decode workload on the GPU, with `rotation` copies of the
+    caches when one call touches less than 1 GiB."""
     d = wl.decode_inputs(cfg)
     q, kc, vc = d["q"].to(dev), d["k_cache"].to(dev), d["v_cache"].to(dev)
     B, Hq, D = q.shape
     ns = cfg.num_splits
-    bufs = dict(q=q, kc=kc, vc=vc, lens=d["seq_lens"].to(dev), sinks=d["sinks"].to(dev), ns=ns,
+    kv = wl.decode_kv_bytes(d["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
+    n = rotation(kv)
+    caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(n - 1)]
+    return dict(q=q, caches=caches, lens=d["seq_lens"].to(dev), sinks=d["sinks"].to(dev), ns=ns,
                 part=(torch.empty(B, Hq, ns, D, device=dev), torch.empty(B, Hq, ns, device=dev),
                       torch.empty(B, Hq, ns, device=dev)),
                 out=torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev),
-                counters=sa.decode_counters(B, Hq, kc.shape[1], 1, dev),
-                kv=wl.decode_kv_bytes(d["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim))
-    return bufs
+                counters=sa.decode_counters(B, Hq, kc.shape[1], 1, dev), kv=kv)
 
 
 def _split_merge(cfg, x):
-    return lambda s: sa.sink_attn_decode(x["q"], x["kc"], x["vc"], x["lens"], x["sinks"],
-                                         cfg.split_size, x["ns"], scale=cfg.scale, out=x["out"],
-                                         partials=x["part"], stream=s)
+    def run(s, i):
+        kc, vc = x["caches"][i % len(x["caches"])]
+        sa.sink_attn_decode(x["q"], kc, vc, x["lens"], x["sinks"], cfg.split_size, x["ns"],
+                            scale=cfg.scale, out=x["out"], partials=x["part"], stream=s)
+    return run
 
 
 def _one_launch(cfg, x):
-    return lambda s: sa.sink_attn_decode_fused(x["q"], x["kc"], x["vc"], x["lens"], x["sinks"],
-                                               cfg.split_size, x["ns"], scale=cfg.scale,
-                                               counters=x["counters"], out=x["out"],
-                                               partials=x["part"], stream=s)
+    def run(s, i):
+        kc, vc = x["caches"][i % len(x["caches"])]
+        sa.sink_attn_decode_fused(x["q"], kc, vc, x["lens"], x["sinks"], cfg.split_size,
+                                  x["ns"], scale=cfg.scale, counters=x["counters"],
+                                  out=x["out"], partials=x["part"], stream=s)
+    return run
 
 
 def ragged_decode_measurement(dev, stream, batch: int, reps: int):
@@ -438,7 +455,7 @@ def ragged_decode_measurement(dev, stream, batch: int, reps: int):
     torch.cuda.empty_cache()
     return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
             "metric": "decode KV GB/s (split + merge, graph replay)", "mean_ms": round(ms, 4),
-            "algorithmic_bytes_per_step": kv,
+            "algorithmic_bytes_per_step": kv, "cache_copies_rotated": rotation(kv),
             "latency_bound": batch < 32,
             "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
@@ -459,6 +476,7 @@ def one_launch_decode_measurement(dev, stream, cfg, reps: int):
     return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
             "metric": "decode KV GB/s, one launch (graph replay)", "mean_ms": round(one, 4),
             "split_merge_ms_same_run": round(two, 4), "algorithmic_bytes_per_step": kv,
+            "cache_copies_rotated": rotation(kv),
             "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 

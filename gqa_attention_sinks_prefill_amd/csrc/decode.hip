@@ -614,10 +614,21 @@ __device__ __forceinline__ void merge_finish(const MergeArgs& a, int row, int la
           }
         k = kMergeRegs;
       }
-      for (; k < cn; ++k) {
-        const float wk = wt(k);
+      // further chunks kMergeRegs at a time: their loads go out together
+      for (; k < cn; k += kMergeRegs) {
+        float ot[kMergeRegs][DL];
 #pragma unroll
-        for (int j = 0; j < DL; ++j) acc[j] += wk * ld(po + (int64_t)(c0 + k) * D + lane + 64 * j);
+        for (int r = 0; r < kMergeRegs; ++r)
+#pragma unroll
+          for (int j = 0; j < DL; ++j)
+            ot[r][j] = k + r < cn ? ld(po + (int64_t)(c0 + k + r) * D + lane + 64 * j) : 0.f;
+#pragma unroll
+        for (int r = 0; r < kMergeRegs; ++r)
+          if (k + r < cn) {
+            const float wk = wt(k + r);
+#pragma unroll
+            for (int j = 0; j < DL; ++j) acc[j] += wk * ot[r][j];
+          }
       }
     }
   }
