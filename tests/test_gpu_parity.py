@@ -75,6 +75,26 @@ def test_prefill_gptoss_shape_sampled_rows():
     assert out.abs().max().item() <= inp["v"].abs().max().item() + 1e-2
 
 
+@pytest.mark.parametrize("n,Hq,Hkv,D", [(32768, 16, 2, 64), (20000, 16, 1, 128)])
+def test_prefill_long_sequence_sampled_rows(n, Hq, Hkv, D):
+    """One sequence four times (D 64) and 2.4 times (D 128) longer than the
+    benchmark shapes: row tiles, key offsets and the per-row key loop far past
+    them, checked on sampled rows (the oracle computes just those)."""
+    cfg = wl.PrefillConfig("long", (n,), 1, None, Hq, Hkv, D, (-4.0, 4.0), seed=230 + D,
+                           edge_sinks={0: float("-inf"), Hq - 1: 20.0})
+    inp = wl.prefill_inputs(cfg)
+    out, lse = _prefill_gpu(inp)
+    assert not torch.isnan(out).any().item(), "unwritten or non-finite outputs"
+    rows = sample_prefill_rows(inp["cu_seqlens"], Hq, n_random=150, seed=230 + D,
+                               all_heads_positions=1)
+    rows = sorted(set(rows) | {(n - 1, h) for h in range(Hq)})
+    o_ref, lse_ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                       inp["cu_seqlens"], causal=True, scale=cfg.scale, rows=rows)
+    assert_close(gather_rows(out, rows), o_ref, what=f"long prefill n={n} D={D}")
+    idx = torch.tensor(rows)
+    assert_lse_close(lse.cpu()[idx[:, 0], idx[:, 1]], lse_ref, what=f"long prefill lse D={D}")
+
+
 def test_prefill_varlen_wide_gqa_d128_sampled_rows():
     cfg = wl.VARLEN_PREFILL
     inp = wl.prefill_inputs(cfg)
@@ -226,6 +246,21 @@ def test_decode_split_size_invariance(split):
     inp = wl.decode_inputs(cfg)
     out, lse, _ = _decode_gpu(inp, split, -(-3000 // split) + 2)     # + 2 empty chunks
     _check_decode(inp, out, lse, f"split {split}")
+
+
+@pytest.mark.parametrize("D,split", [(64, 4096), (128, 2048)])
+def test_decode_very_long_context(D, split):
+    """Contexts of 100k-131k tokens (4x the ragged benchmark's longest): cache
+    offsets far past the benchmark shapes, 32-64 chunks per request; split +
+    merge and the one-launch call both against the oracle on every row."""
+    cfg = wl.DecodeConfig("long", 2, None, (100000, 131072), 131072, 16, 2, D, (-4.0, 4.0),
+                          split_size=split, seed=231 + D, edge_sinks={3: float("-inf")})
+    inp = wl.decode_inputs(cfg)
+    out, lse, _ = _decode_gpu(inp, split)
+    _check_decode(inp, out, lse, f"131k-token decode D={D}")
+    out_f, lse_f, _ = _fused_gpu(inp, split)
+    assert torch.equal(out_f[:, 0].view(torch.int16), out.view(torch.int16))
+    assert torch.equal(lse_f[:, 0], lse)
 
 
 def test_decode_edge_lengths():
