@@ -99,6 +99,11 @@ struct KvAppendArgs {
 int prefill_heads_per_workgroup(int group);
 int prefill_rows_per_workgroup(int group, int head_dim);
 
+// one instantiation each (prefill_d64.hip, prefill_d128.hip)
+hipError_t launch_prefill_d64(const PrefillArgs& a, int heads_per_wg, int64_t num_blocks,
+                              hipStream_t stream);
+hipError_t launch_prefill_d128(const PrefillArgs& a, int heads_per_wg, int64_t num_blocks,
+                               hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int64_t num_blocks,
                           hipStream_t stream);
 // Blocks of 16 columns one decode workgroup serves (1, 2, or up to 4 for head_dim 64).
