@@ -501,8 +501,10 @@ def main():
                     help="untimed steps first; the clocks take some 20 ms of load to settle")
     ap.add_argument("--cpu-seconds", type=float, default=45.0,
                     help="host time budget of the oracle baseline (0 disables it)")
-    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
-                    help="launch only one part of the step (for hardware-counter runs)")
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "varlen", "ragged"),
+                    default="all",
+                    help="launch only one part of the step, or only the head_dim 128 varlen "
+                         "prefill / the B = 128 ragged decode (for hardware-counter runs)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra wide-GQA varlen (head_dim 128) prefill measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -520,6 +522,13 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     if args.copy_calibration:
         copy_calibration(dev, args.steps)
+        return
+    if args.only in ("varlen", "ragged"):
+        stream = torch.cuda.current_stream()
+        line = (varlen_prefill_measurement(dev, stream, args.steps) if args.only == "varlen"
+                else ragged_decode_measurement(dev, stream, 128, args.steps))
+        line["note"] = f"--only {args.only}: this workload alone"
+        print(json.dumps(line), flush=True)
         return
 
     # ---- inputs, resident in HBM before timing ---------------------------------
