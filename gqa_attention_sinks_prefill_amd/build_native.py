@@ -20,6 +20,9 @@ SOURCES = ["api.cpp", "prefill.hip", "prefill_d64.hip", "prefill_d128.hip", "dec
 # scheduled with LLVM's iterative ILP machine scheduler: 3% faster on the
 # GPT-OSS-shaped prefill in interleaved A/B runs, same output bits; the
 # head_dim 128 one ran 1% slower with it and keeps the default.
+# The iterative scheduler is marked experimental in LLVM (with -g it crashes on
+# this kernel), so a source whose extra flags fail to compile is built again
+# without them.
 SOURCE_FLAGS = {"prefill_d64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 PROBE_LIB = os.path.join(PKG, "libhbmprobe.so")
 PROBE_SOURCES = ["hbm_read_probe.hip"]
@@ -33,13 +36,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libsinkattn.so)")
 
 
-def compile_command(src: str, obj: str) -> list[str]:
+def compile_command(src: str, obj: str, extra: bool = True) -> list[str]:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
             # packed fp32 VALU ops are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-result",
-            f"-I{INCLUDE}", f"-I{CSRC}"] + SOURCE_FLAGS.get(src, []) + [
+            f"-I{INCLUDE}", f"-I{CSRC}"] + (SOURCE_FLAGS.get(src, []) if extra else []) + [
             "-o", obj, os.path.join(CSRC, src)]
+
+
+def _compile_source(src: str, obj: str, verbose: bool) -> None:
+    try:
+        _run(compile_command(src, obj), verbose)
+    except RuntimeError as err:
+        if not SOURCE_FLAGS.get(src):
+            raise
+        print(f"note: {src} failed with {' '.join(SOURCE_FLAGS[src])}; building it without "
+              f"them\n{str(err)[-400:]}", file=sys.stderr)
+        _run(compile_command(src, obj, extra=False), verbose)
 
 
 def link_command(out: str, objs) -> list[str]:
@@ -69,7 +83,7 @@ def _compile(lib: str, sources, verbose: bool) -> str:
     with tempfile.TemporaryDirectory(prefix="sinkattn_build_") as tmpdir:
         objs = [os.path.join(tmpdir, os.path.splitext(s)[0] + ".o") for s in sources]
         with ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
-            list(ex.map(lambda so: _run(compile_command(*so), verbose), zip(sources, objs)))
+            list(ex.map(lambda so: _compile_source(so[0], so[1], verbose), zip(sources, objs)))
         tmp = lib + ".tmp"
         _run(link_command(tmp, objs), verbose)
     os.replace(tmp, lib)
