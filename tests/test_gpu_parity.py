@@ -126,6 +126,21 @@ def test_prefill_ragged_edges_all_rows(Hq, Hkv, D, causal):
     assert_lse_close(lse.reshape(-1), lse_ref, what="ragged prefill lse")
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(12, 4), (12, 2), (24, 2), (40, 8)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_odd_gqa_groups_all_rows(Hq, Hkv, D):
+    """GQA groups of 3, 6, 12 and 5: one, two or four heads per workgroup, and
+    head-group counts on either side of a multiple of the 8 XCDs."""
+    lens = [40, 0, 97, 130]
+    inp = _prefill_case(lens, Hq, Hkv, D, seed=300 + Hq + Hkv + D,
+                        edges={1: float("-inf"), Hq - 1: 20.0})
+    out, lse = _prefill_gpu(inp, causal=True)
+    o_ref, lse_ref, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                       inp["cu_seqlens"], causal=True, scale=1 / math.sqrt(D))
+    assert_close(out.reshape(-1, D), o_ref, what=f"prefill Hq={Hq} Hkv={Hkv} D={D}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what=f"prefill lse Hq={Hq} Hkv={Hkv}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_growing_logits_all_rows(D, causal):
@@ -290,6 +305,24 @@ def test_decode_head_dims_and_groups(Hq, Hkv, D):
     _check_decode(inp, out, lse, f"decode Hq={Hq} Hkv={Hkv} D={D}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_nhd_cache_layout(D):
+    """Token-major caches [B, max_ctx, Hkv, D] passed as strided [B, Hkv,
+    max_ctx, D] views (token stride Hkv * D, head stride D): split + merge
+    against the oracle, the one-launch call bitwise against it."""
+    cfg = wl.DecodeConfig("nhd", 4, None, (1, 1500), 1536, 16, 4, D, (-4.0, 4.0),
+                          split_size=512, seed=320 + D, edge_sinks={2: float("-inf")})
+    inp = wl.decode_inputs(cfg)
+    nhd = lambda t: t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+    kn, vn = nhd(inp["k_cache"]), nhd(inp["v_cache"])
+    assert kn.stride(2) == 4 * D and kn.stride(1) == D
+    out, lse, _ = _decode_gpu(dict(inp, k_cache=kn, v_cache=vn), 512)
+    _check_decode(inp, out, lse, f"NHD-cache decode D={D}")
+    out_f, lse_f, _ = _fused_gpu(dict(inp, k_cache=kn, v_cache=vn), 512)
+    assert torch.equal(out_f[:, 0].view(torch.int16), out.view(torch.int16))
+    assert torch.equal(lse_f[:, 0], lse)
+
+
 def test_decode_strided_query_and_output():
     """Non-contiguous q / out views with head stride != D."""
     cfg = wl.DecodeConfig("strided", 3, None, (100, 900), 1024, 8, 2, 64, (-4.0, 4.0),
@@ -351,6 +384,22 @@ def test_decode_multi_all_rows(q_len, Hq, Hkv, D):
                                             inp["seq_lens"], inp["sinks"])
     assert_close(out.reshape(-1, D), o_ref, what=f"multi decode q_len={q_len} Hq={Hq} D={D}")
     assert_lse_close(lse.reshape(-1), lse_ref, what="multi decode lse")
+
+
+@pytest.mark.parametrize("Hq,Hkv,q_len", [(12, 4, 1), (12, 4, 3), (40, 8, 2), (24, 4, 5)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_odd_gqa_groups_all_rows(Hq, Hkv, q_len, D):
+    """GQA groups of 3, 5 and 6 with 1-5 new tokens: 3 to 30 (token, head)
+    columns per KV head, partly filled 16-column blocks."""
+    lens = [0, 1, q_len, 300, 1100]
+    inp = _multi_cfg(lens, q_len, Hq, Hkv, D, seed=330 + Hq + q_len + D, split=256,
+                     edges={0: float("-inf"), Hq - 1: 20.0})
+    inp = dict(inp, q=_q4(inp["q"]))        # [B, q_len, Hq, D] also for q_len = 1
+    out, lse = _decode_multi_gpu(inp, 256)
+    o_ref, lse_ref, _ = oracle.decode_multi(inp["q"], inp["k_cache"], inp["v_cache"],
+                                            inp["seq_lens"], inp["sinks"])
+    assert_close(out.reshape(-1, D), o_ref, what=f"decode Hq={Hq} Hkv={Hkv} q_len={q_len} D={D}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="odd-group decode lse")
 
 
 @pytest.mark.parametrize("q_len", [8, 16])
