@@ -854,6 +854,29 @@ def _paged_ref(inp, kp, vp, bt, P, fp8, rows=None):
                                      inp["sinks"], rows=rows, **sc)
 
 
+@pytest.mark.parametrize("Hq,Hkv,q_len,D", [(12, 4, 1, 64), (12, 4, 3, 128), (40, 8, 2, 64)])
+def test_decode_fp8_odd_gqa_groups_all_rows(Hq, Hkv, q_len, D):
+    """FP8 caches with GQA groups of 3 and 5 (partly filled column blocks)."""
+    lens = [0, q_len, 70, 300, 1100]
+    inp = _fp8_cfg(lens, q_len, Hq, Hkv, D, seed=340 + Hq + q_len + D, split=256,
+                   edges={0: float("-inf"), Hq - 1: 20.0})
+    out, lse, _ = _fp8_gpu(inp, 256)
+    o_ref, lse_ref, _ = _fp8_ref(inp)
+    assert_close(out.reshape(-1, D), o_ref, what=f"fp8 decode Hq={Hq} Hkv={Hkv} q_len={q_len}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="fp8 odd-group decode lse")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_paged_odd_gqa_group_all_rows(fp8):
+    """Pages of 16 tokens with a GQA group of 3 and 2 new tokens."""
+    lens = [2, 33, 200, 0]
+    inp, kp, vp, bt = _paged_case(lens, 2, 12, 4, 64, 16, fp8, seed=350 + fp8, max_ctx=256)
+    out, lse, _ = _paged_gpu(inp, kp, vp, bt, 64, fp8)
+    o_ref, lse_ref, _ = _paged_ref(inp, kp, vp, bt, 16, fp8)
+    assert_close(out.reshape(-1, 64), o_ref, what=f"paged decode group 3 fp8={fp8}")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="paged odd-group decode lse")
+
+
 @pytest.mark.parametrize("P,fp8,q_len,D", [(16, False, 1, 64), (16, True, 1, 64),
                                            (64, False, 3, 64), (256, True, 2, 64),
                                            (16, False, 1, 128), (32, True, 4, 128)])
