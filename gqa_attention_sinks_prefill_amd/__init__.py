@@ -7,10 +7,17 @@ the current HIP stream, and turns a non-zero return code into an exception.
 PyTorch is used for device memory and streams only.
 
 Entry points (same names as the C ABI):
-  sink_attn_prefill(q, k, v, sinks, cu_seqlens, max_seqlen, ...)
-  sink_attn_decode_split(q, k_cache, v_cache, seq_lens, sinks, split_size, ...)
-  sink_attn_merge_states(part_o, part_m, part_d, ...)
-and the convenience wrapper sink_attn_decode (split + merge on one stream).
+  prefill      sink_attn_prefill (causal / non-causal varlen),
+               sink_attn_prefill_chunked (queries at the end of a longer key range)
+  decode       sink_attn_decode_split (chunk states), sink_attn_merge_states,
+               sink_attn_decode_multi_split (q_len new tokens per request),
+               sink_attn_decode_multi_split_fp8 (FP8 E4M3 caches),
+               sink_attn_decode_paged_split (block-table pages, bf16 or FP8),
+               sink_attn_decode_fused (split and merge in one launch; counters from
+               decode_counters)
+  KV cache     sink_attn_kv_append, sink_attn_kv_append_fp8, sink_attn_kv_append_paged
+and the wrappers sink_attn_decode, sink_attn_decode_multi, sink_attn_decode_fp8 and
+sink_attn_decode_paged (split + merge on one stream).
 """
 from __future__ import annotations
 
