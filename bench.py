@@ -502,11 +502,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=45.0,
                     help="host time budget of the oracle baseline (0 disables it)")
     ap.add_argument("--only", choices=("all", "prefill", "decode", "varlen", "ragged", "mtp",
-                                       "fp8"),
+                                       "fp8", "read"),
                     default="all",
                     help="launch only one part of the step, or only the head_dim 128 varlen "
                          "prefill / the B = 128 ragged decode / the multi-token decode / the "
-                         "FP8-cache decode (for hardware-counter runs)")
+                         "FP8-cache decode / the streaming-read reference (for hardware-counter "
+                         "runs)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra wide-GQA varlen (head_dim 128) prefill measurement")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -525,12 +526,13 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev, args.steps)
         return
-    if args.only in ("varlen", "ragged", "mtp", "fp8"):
+    if args.only in ("varlen", "ragged", "mtp", "fp8", "read"):
         stream = torch.cuda.current_stream()
         line = {"varlen": lambda: varlen_prefill_measurement(dev, stream, args.steps),
                 "ragged": lambda: ragged_decode_measurement(dev, stream, 128, args.steps),
                 "mtp": lambda: multi_decode_measurement(dev, stream, args.steps),
-                "fp8": lambda: fp8_decode_measurement(dev, stream, args.steps)}[args.only]()
+                "fp8": lambda: fp8_decode_measurement(dev, stream, args.steps),
+                "read": lambda: hbm_read_reference(dev, stream, max(3, args.steps))}[args.only]()
         line["note"] = f"--only {args.only}: this workload alone"
         print(json.dumps(line), flush=True)
         return
