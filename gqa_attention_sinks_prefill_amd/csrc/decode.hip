@@ -670,8 +670,11 @@ __device__ __forceinline__ void decode_merge_if_last(const DecodeArgs& a, int un
                                               ((int64_t)len + a.split_size - 1) / a.split_size));
   if (c >= live) return;
   int32_t* counter = a.counters + ((int64_t)b * a.num_kv_heads + g) * a.head_slices + hs;
+  // The first barrier's fence keeps the compiler from moving the state stores
+  // below the wait; the wait makes each wave's device-scope stores complete;
+  // the second barrier makes them all complete before thread 0 counts in.
   __syncthreads();
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // every wave's state stores acknowledged
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   if (threadIdx.x == 0) is_last = atomicAdd(counter, 1) == live - 1;
   __syncthreads();
