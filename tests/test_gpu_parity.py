@@ -466,6 +466,7 @@ _EDGE_LENS = [0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 447, 448, 511
     (24, 8, 64, 3, 128),      # two blocks, 768 chunks: two waves per chunk
     (32, 8, 64, 8, 128),      # 64 columns (four blocks), 1024 chunks: a wave per chunk
     (64, 8, 128, 1, 128),     # head_dim 128, 2048 chunks: a wave per chunk
+    (1040, 8, 64, 1, 64),     # over a thousand requests, 66560 units, most chunks empty
 ])
 def test_decode_work_splits_edge_lengths(B, Hkv, D, q_len, split):
     """Each way a chunk is shared by waves (one, two or four per chunk), at
