@@ -40,8 +40,9 @@
 // codes with a scale per KV head (converted exactly to bf16 in registers;
 // V through the 8-bit transposing read), and pages behind a block table (a
 // buffer resource per 16-key block).
-// merge_kernel: one wave per (b, h) row, lane = d; log-sum-exp weighted sum of
-// the chunk states, rounded to bf16.
+// merge_rows_kernel (up to 16 chunks) and merge_kernel: log-sum-exp weighted
+// sum of the chunk states, rounded to bf16 -- D / 4 lanes per (b, h) row, or
+// one wave per row with lane = d.
 #include "device_common.h"
 #include "launch.h"
 
@@ -720,6 +721,91 @@ __global__ __launch_bounds__(64 * W, (D == 64 && CB <= 2) ? 2 : 1) void decode_s
   if (a.counters != nullptr) decode_merge_if_last<D, CB, W>(a, blockIdx.x);
 }
 
+// The merge of split decode into at most kMergeBlock chunks: D / 4 lanes per
+// row (four d each, 16-byte loads), 64 / (D / 4) rows per wave.  Each lane
+// loads its row's (m, d) of every chunk itself (the lanes of a row share those
+// addresses), so the merge needs no lane exchange and all its loads go out at
+// once.  The sums run in merge_finish's order -- o chunk by chunk, sum_c w_c
+// as the pairwise tree that its butterfly reduction forms -- so both merges
+// give the same bits.  Needs part_o 16-byte aligned.  (Against merge_kernel:
+// 64 x 64 rows of 8 chunks 3.5 vs 4.0 us, 16384 rows 7.7 vs 10.8 us; past 16
+// chunks, in blocks of 16, it was slower and merge_kernel stays.)
+constexpr int kMergeBlock = 16;
+
+__device__ __forceinline__ float tree_sum16(const float (&w)[kMergeBlock]) {
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = w[2 * i] + w[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+  return (t[0] + t[1]) + (t[2] + t[3]);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_rows_kernel(MergeArgs a) {
+  constexpr int LPR = D / 4;                  // lanes per row
+  constexpr int RPW = 64 / LPR;               // rows per wave
+  constexpr int NB = kMergeBlock;
+  const int lane = threadIdx.x & 63;
+  const int row = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  if (row >= a.rows) return;
+  const int d0 = 4 * (lane % LPR);
+  const int ns = a.num_splits;
+  const int64_t first = (int64_t)row * ns;
+  const float* pm = a.part_m + first;
+  const float* pd = a.part_d + first;
+  const float* po = a.part_o + first * D + d0;
+  // loads clamped to the last chunk (always issued, no branch around them),
+  // chunks past it given m = -inf
+  float mv[NB], dv[NB], w[NB];
+  f32x4_t ov[NB];
+  auto load_block = [&] {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int ci = min(i, ns - 1);
+      mv[i] = pm[ci];
+      dv[i] = pd[ci];
+      ov[i] = *reinterpret_cast<const f32x4_t*>(po + (int64_t)ci * D);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      if (i >= ns) mv[i] = -INFINITY;
+  };
+  // the weights and o, chunk by chunk; returns the tree sum of the weights
+  // (the chunks past ns add exact zeros to it)
+  auto combine = [&](float M, f32x4_t& acc) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      w[i] = mv[i] == -INFINITY ? 0.f : dv[i] * fast_exp2((mv[i] - M) * kLog2e);
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      if (i < ns) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += w[i] * ov[i][j];
+      }
+    return tree_sum16(w);
+  };
+  // one round trip: all of the row's chunks in registers
+  load_block();
+  float M = -INFINITY, W = 0.f;
+  f32x4_t acc = {};
+#pragma unroll
+  for (int i = 0; i < NB; ++i) M = fmaxf(M, mv[i]);
+  if (M != -INFINITY) W = combine(M, acc);
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  const int bt = row / a.num_q_heads, h = row % a.num_q_heads;
+  uint16_t* op = a.o + (int64_t)(bt / a.q_len) * a.o_sb + (int64_t)(bt % a.q_len) * a.o_st +
+                 (int64_t)h * a.o_sh + d0;
+  uint32_t pk[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const __bf16 lo = (__bf16)(acc[2 * j] * inv), hi = (__bf16)(acc[2 * j + 1] * inv);
+    pk[j] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+  *reinterpret_cast<uint2*>(op) = make_uint2(pk[0], pk[1]);
+  if (a.lse != nullptr && d0 == 0) a.lse[row] = W > 0.f ? M + __logf(W) : -INFINITY;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -793,7 +879,17 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_bl
 }
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(kThreads);
+  const dim3 block(kThreads);
+  if (a.num_splits <= kMergeBlock && reinterpret_cast<uintptr_t>(a.part_o) % 16 == 0) {
+    const int rows_per_block = (kThreads / 64) * (64 / (head_dim / 4));
+    const dim3 grid((unsigned)((a.rows + rows_per_block - 1) / rows_per_block));
+    if (head_dim == 64)
+      hipLaunchKernelGGL(merge_rows_kernel<64>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(merge_rows_kernel<128>, grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((a.rows + 3) / 4));
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, a);
   else

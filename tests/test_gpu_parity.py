@@ -1129,3 +1129,50 @@ def test_decode_and_prefill_replay_from_a_captured_graph():
     o_ref, _, _ = oracle.decode(q_d.cpu(), dec["k_cache"], dec["v_cache"], dec["seq_lens"],
                                 dec["sinks"])
     assert_close(o_d.cpu().reshape(-1, 64), o_ref, what="decode after graph replays")
+
+
+def _merge_inputs(B, Hq, ns, D, seed):
+    """Chunk states with the cases a merge meets: chunks with m = -inf and d = 0
+    (past a request's end), rows with no weight at all, a wide spread of m and
+    chunks with d = 0 but a finite m."""
+    g = torch.Generator().manual_seed(seed)
+    po = torch.randn(B, Hq, ns, D, generator=g)
+    pm = torch.randn(B, Hq, ns, generator=g) * 8
+    pd = torch.rand(B, Hq, ns, generator=g) * 50
+    empty = torch.rand(B, Hq, ns, generator=g) < 0.4
+    pm[empty], pd[empty], po[empty] = float("-inf"), 0.0, 0.0
+    pm[0, 0], pd[0, 0], po[0, 0] = float("-inf"), 0.0, 0.0          # a row with no weight
+    pd[0, 1, 0] = 0.0                                                 # d = 0, finite m
+    return po, pm, pd
+
+
+@pytest.mark.parametrize("ns", [1, 7, 16, 17, 40, 100])
+@pytest.mark.parametrize("D", [64, 128])
+def test_merge_states_against_the_oracle(ns, D):
+    """sink_attn_merge_states on adversarial chunk states (up to 16 chunks and
+    past it) against the oracle's fp64 merge; and, from a part_o that is only
+    4-byte aligned, the same bits."""
+    B, Hq = 3, 40
+    po, pm, pd = _merge_inputs(B, Hq, ns, D, seed=500 + ns + D)
+    o_ref, lse_ref = oracle.merge_states(po.reshape(-1, ns, D).double().numpy(),
+                                         pm.reshape(-1, ns).double().numpy(),
+                                         pd.reshape(-1, ns).double().numpy())
+    g_po, g_pm, g_pd = po.to(DEV), pm.to(DEV), pd.to(DEV)
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, Hq), float("nan"), device=DEV)
+    sa.sink_attn_merge_states(g_po, g_pm, g_pd, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert_close(out.reshape(-1, D), o_ref, what=f"merge ns={ns} D={D}")
+    lse_h = lse.reshape(-1).cpu()
+    assert torch.isneginf(lse_h[0]) and torch.all(out[0, 0].float() == 0)
+    assert_lse_close(lse_h, lse_ref, what=f"merge ns={ns} D={D} lse")
+    # part_o one float past a 16-byte boundary
+    buf = torch.empty(po.numel() + 1, device=DEV)
+    g_po2 = buf[1:].view(po.shape)
+    g_po2.copy_(g_po)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    sa.sink_attn_merge_states(g_po2, g_pm, g_pd, out=out2, lse=lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(lse2, lse)
