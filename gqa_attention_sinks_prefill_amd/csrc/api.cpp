@@ -148,7 +148,7 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
                               float* part_o, float* part_m, float* part_d, void* stream,
                               int32_t* counters = nullptr, void* o = nullptr, int64_t o_stride_b = 0,
                               int64_t o_stride_tok = 0, int64_t o_stride_head = 0,
-                              float* lse = nullptr) {
+                              float* lse = nullptr, bool merged = false) {
   const bool fp8 = k_scale != nullptr || v_scale != nullptr;
   const bool fused = counters != nullptr || o != nullptr;
   const bool paged = page_size != 0;
@@ -181,8 +181,8 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
   if (paged && !aligned(block_tables, 4))
     return fail(SINK_ATTN_EINVAL, "block_tables must be 4-byte aligned");
   if (fused) {
-    if (!counters || !o) return fail(SINK_ATTN_EINVAL, "a required pointer is null");
-    if (!aligned(counters, 4) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
+    if ((!merged && !counters) || !o) return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+    if ((!merged && !aligned(counters, 4)) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
       return fail(SINK_ATTN_EINVAL, "counters and lse must be 4-byte aligned, o 16-byte aligned");
     if (!stride_ok(o_stride_b) || !stride_ok(o_stride_tok) || !stride_ok(o_stride_head))
       return fail(SINK_ATTN_EINVAL, "output strides must be non-negative multiples of 8 elements");
@@ -246,8 +246,9 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
   a.split_size = split_size;
   a.num_splits = num_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.skip_empty = merged ? 1 : 0;
   if (fused) {
-    a.counters = counters;
+    a.counters = merged ? nullptr : counters;
     a.merge.part_o = part_o;
     a.merge.part_m = part_m;
     a.merge.part_d = part_d;
@@ -261,8 +262,14 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
     a.merge.num_q_heads = num_q_heads;
     a.merge.num_splits = num_splits;
   }
-  return launched(sinkattn::launch_decode_split(a, head_dim, num_blocks, static_cast<hipStream_t>(stream)),
-                  "decode_split");
+  const int rc = launched(sinkattn::launch_decode_split(a, head_dim, num_blocks,
+                                                        static_cast<hipStream_t>(stream)),
+                          "decode_split");
+  if (rc != SINK_ATTN_OK || !merged) return rc;
+  a.merge.seq_lens = seq_lens;
+  a.merge.split_size = split_size;
+  return launched(sinkattn::launch_merge(a.merge, head_dim, static_cast<hipStream_t>(stream)),
+                  "merge_states");
 }
 
 int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
@@ -320,6 +327,27 @@ int sink_attn_decode_fused(const void* q, int64_t q_stride_b, int64_t q_stride_t
                             0, seq_lens, batch, max_ctx, sinks, num_q_heads, num_kv_heads,
                             head_dim, scale, split_size, num_splits, part_o, part_m, part_d,
                             stream, counters, o, o_stride_b, o_stride_tok, o_stride_head, lse);
+}
+
+int sink_attn_decode_merged(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                            int64_t q_stride_head, int32_t q_len, const void* k_cache,
+                            const void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
+                            int64_t kv_stride_tok, const float* k_scale, const float* v_scale,
+                            const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                            const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, float scale, int32_t split_size, int32_t num_splits,
+                            float* part_o, float* part_m, float* part_d, void* o,
+                            int64_t o_stride_b, int64_t o_stride_tok, int64_t o_stride_head,
+                            float* lse, void* stream) {
+  g_err[0] = '\0';
+  if ((k_scale == nullptr) != (v_scale == nullptr))
+    return fail(SINK_ATTN_EINVAL, "k_scale and v_scale must both be given or both be null");
+  if (batch > 0 && !o) return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  return decode_multi_split(q, q_stride_b, q_stride_tok, q_stride_head, q_len, k_cache, v_cache,
+                            kv_stride_b, kv_stride_head, kv_stride_tok, k_scale, v_scale, nullptr, 0,
+                            0, seq_lens, batch, max_ctx, sinks, num_q_heads, num_kv_heads,
+                            head_dim, scale, split_size, num_splits, part_o, part_m, part_d,
+                            stream, nullptr, o, o_stride_b, o_stride_tok, o_stride_head, lse, true);
 }
 
 int sink_attn_decode_paged_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,

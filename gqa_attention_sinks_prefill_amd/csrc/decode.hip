@@ -193,7 +193,7 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int unit, uint1
   // (In one launch the merge stops at the request's last chunk with keys, so
   // there such chunks write nothing.)
   if (n == 0 && c != 0) {
-    if (dev_scope) return;
+    if (dev_scope || a.skip_empty) return;
     for (int item = tid; item < nx * D; item += kBlock) {
       const int64_t row = out_row(x0 + item / D);
       const int d = item % D;
@@ -732,6 +732,16 @@ __global__ __launch_bounds__(64 * W, (D == 64 && CB <= 2) ? 2 : 1) void decode_s
 // chunks, in blocks of 16, it was slower and merge_kernel stays.)
 constexpr int kMergeBlock = 16;
 
+// Chunks of row (b * q_len + t) * num_q_heads + h to merge: all, or with the
+// request lengths given, those holding keys (chunk 0 at least) -- the split
+// decode then wrote no state for the others, whose (0, -inf, 0) adds only
+// exact zeros to a merge.
+__device__ __forceinline__ int merge_chunks(const MergeArgs& a, int row) {
+  if (a.seq_lens == nullptr) return a.num_splits;
+  const int64_t len = a.seq_lens[row / (a.q_len * a.num_q_heads)];
+  return (int)max((int64_t)1, min((int64_t)a.num_splits, (len + a.split_size - 1) / a.split_size));
+}
+
 __device__ __forceinline__ float tree_sum16(const float (&w)[kMergeBlock]) {
   float t[8];
 #pragma unroll
@@ -750,8 +760,8 @@ __global__ __launch_bounds__(kThreads) void merge_rows_kernel(MergeArgs a) {
   const int row = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * RPW + lane / LPR;
   if (row >= a.rows) return;
   const int d0 = 4 * (lane % LPR);
-  const int ns = a.num_splits;
-  const int64_t first = (int64_t)row * ns;
+  const int ns = merge_chunks(a, row);
+  const int64_t first = (int64_t)row * a.num_splits;
   const float* pm = a.part_m + first;
   const float* pd = a.part_d + first;
   const float* po = a.part_o + first * D + d0;
@@ -810,9 +820,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
+  const int ns = merge_chunks(a, row);
   MergeIn<D> in;
-  merge_load<D, false>(a, row, threadIdx.x & 63, a.num_splits, in);
-  merge_finish<D, false>(a, row, threadIdx.x & 63, a.num_splits, in);
+  merge_load<D, false>(a, row, threadIdx.x & 63, ns, in);
+  merge_finish<D, false>(a, row, threadIdx.x & 63, ns, in);
 }
 
 }  // namespace

@@ -39,6 +39,10 @@ struct MergeArgs {
   int32_t q_len;          // new tokens per request (1 for plain decode)
   int32_t num_q_heads;
   int32_t num_splits;
+  // Null: merge num_splits chunks per row.  Else the request lengths: merge
+  // only the chunks that hold keys (chunk 0 at least) of each row's request.
+  const int32_t* seq_lens;
+  int32_t split_size;
 };
 
 struct DecodeArgs {
@@ -73,6 +77,9 @@ struct DecodeArgs {
   // completes a slice's last chunk merges its rows into merge.o / merge.lse.
   int32_t* counters;
   MergeArgs merge;
+  // Chunks past a request's end write no state (a merge given the lengths
+  // follows).
+  int32_t skip_empty;
 };
 
 

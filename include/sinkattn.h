@@ -270,6 +270,35 @@ int sink_attn_decode_fused(const void* q, int64_t q_stride_b, int64_t q_stride_t
                            int64_t o_stride_head, float* lse, void* stream);
 
 /*
+ * Split decode and merge for ragged batches, in two launches: as
+ * sink_attn_decode_multi_split followed by sink_attn_merge_states, except
+ * that chunks past a request's end (chunk index >= max(1, ceil(seq_lens[b] /
+ * split_size))) write no state and the merge stops at each request's last
+ * chunk with keys -- their state (0, -inf, 0) would add only exact zeros, so
+ * o and lse are bitwise those of the two calls.  Writing those states is
+ * what chunks past the end cost in a ragged batch ("Hosting Qwen on
+ * Blackwell", section "Decoders": decode is bound by memory traffic).
+ *   Arguments as sink_attn_decode_fused without counters: part_o / part_m /
+ *   part_d [B, q_len, Hq, num_splits(, D)] fp32 caller-allocated scratch
+ *   (entries of chunks past a request's end are left as they were); o
+ *   [B, q_len, Hq, D] bf16 (output, 16-byte aligned, strides multiples of 8
+ *   elements); lse NULL or fp32 [B, q_len, Hq] (output).  k_scale / v_scale:
+ *   both NULL (bf16 caches) or both given (FP8 E4M3 codes, as
+ *   sink_attn_decode_multi_split_fp8).
+ * Errors: as sink_attn_decode_fused (no counters to check).
+ */
+int sink_attn_decode_merged(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                            int64_t q_stride_head, int32_t q_len, const void* k_cache,
+                            const void* v_cache, int64_t kv_stride_b, int64_t kv_stride_head,
+                            int64_t kv_stride_tok, const float* k_scale, const float* v_scale,
+                            const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                            const float* sinks, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, float scale, int32_t split_size, int32_t num_splits,
+                            float* part_o, float* part_m, float* part_d, void* o,
+                            int64_t o_stride_b, int64_t o_stride_tok, int64_t o_stride_head,
+                            float* lse, void* stream);
+
+/*
  * FP8 KV cache.  The pages speak of FP8 only for weights; decode, though, is
  * bound by the bytes of the cache it streams ("Hosting Qwen on Blackwell",
  * section "Decoders"), and one byte per element halves them.  Format: OCP FP8

@@ -447,3 +447,39 @@ def test_python_binding_requires_gpu_tensors():
     q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         sa.sink_attn_prefill(q, q, q, torch.zeros(2), torch.zeros(2, dtype=torch.int32), 4)
+
+
+def _decode_merged(**kw):
+    a = dict(q=16, q_sb=4 * 4096, q_st=4096, q_sh=64, q_len=4, k=16, v=16,
+             kv_sb=8 * 1024 * 64, kv_sh=1024 * 64, kv_st=64, ks=None, vs=None, lens=4, batch=4,
+             max_ctx=1024, sinks=4, hq=64, hkv=8, d=64, scale=0.125, split=256, nsplit=4, po=4,
+             pm=4, pd=4, o=32, o_sb=4 * 4096, o_st=4096, o_sh=64, lse=None)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_decode_merged(
+        a["q"], a["q_sb"], a["q_st"], a["q_sh"], a["q_len"], a["k"], a["v"], a["kv_sb"],
+        a["kv_sh"], a["kv_st"], a["ks"], a["vs"], a["lens"], a["batch"], a["max_ctx"],
+        a["sinks"], a["hq"], a["hkv"], a["d"], a["scale"], a["split"], a["nsplit"], a["po"],
+        a["pm"], a["pd"], a["o"], a["o_sb"], a["o_st"], a["o_sh"], a["lse"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ks=4), -1, "both"),
+    (dict(o=None), -1, "null"),
+    (dict(o=40), -1, "aligned"),
+    (dict(lse=6), -1, "aligned"),
+    (dict(o_st=100), -1, "multiples of 8"),
+    (dict(q_len=0), -1, "q_len"),
+    (dict(nsplit=2), -1, "cover"),
+    (dict(d=32), -2, "head_dim"),
+])
+def test_decode_merged_rejects_bad_arguments(kw, code, needle):
+    rc, msg = _decode_merged(**kw)
+    assert rc == code and needle in msg, (rc, msg)
+
+
+def test_decode_merged_empty_batch_is_a_noop():
+    rc, msg = _decode_merged(batch=0, q=None, k=None, v=None, lens=None, sinks=None, po=None,
+                             pm=None, pd=None, o=None)
+    assert rc == 0, msg

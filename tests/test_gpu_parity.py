@@ -1176,3 +1176,56 @@ def test_merge_states_against_the_oracle(ns, D):
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert torch.equal(lse2, lse)
+
+
+# ------------------------------------------ split + length-aware merge --
+def _merged_gpu(inp, split, *, fp8=False):
+    q = _q4(inp["q"]).to(DEV)
+    kc, vc = inp["k_cache"].to(DEV), inp["v_cache"].to(DEV)
+    B, q_len, Hq, D = q.shape
+    ns = -(-kc.shape[2] // split)
+    po = torch.full((B, q_len, Hq, ns, D), float("nan"), device=DEV)
+    pm = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    pd = torch.full((B, q_len, Hq, ns), float("nan"), device=DEV)
+    out = torch.full((B, q_len, Hq, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, q_len, Hq), float("nan"), device=DEV)
+    kw = dict(k_scale=inp["k_scale"].to(DEV), v_scale=inp["v_scale"].to(DEV)) if fp8 else {}
+    sa.sink_attn_decode_merged(q, kc, vc, inp["seq_lens"].to(DEV), inp["sinks"].to(DEV), split,
+                               ns, out=out, lse=lse, partials=(po, pm, pd), **kw)
+    torch.cuda.synchronize()
+    return out, lse, (po, pm, pd)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("case", range(len(_FUSED_CASES)))
+def test_decode_merged_is_bitwise_split_then_merge(case, fp8):
+    """Split decode whose chunks past a request's end write nothing, merged
+    over the chunks that hold keys: bitwise the output and lse of split decode
+    + sink_attn_merge_states (the partials start as NaN, so a chunk state the
+    merge read without it being written would show); every wave split."""
+    lens, q_len, Hq, Hkv, D, split = _FUSED_CASES[case]
+    mk = _fp8_cfg if fp8 else _multi_cfg
+    inp = mk(lens, q_len, Hq, Hkv, D, seed=290 + case, split=split,
+             edges={0: float("-inf"), Hq - 1: 20.0})
+    out_m, lse_m, (po, pm, pd) = _merged_gpu(inp, split, fp8=fp8)
+    out_s, lse_s = _split_merge_gpu(inp, split, fp8)
+    assert _bitwise(out_m, out_s), f"merged output differs from split+merge, case {case}"
+    assert torch.equal(lse_m, lse_s), f"merged lse differs from split+merge, case {case}"
+    # chunks past each request's end were left untouched (still NaN)
+    ns = pm.shape[-1]
+    for b, L in enumerate(lens):
+        live = max(1, min(ns, -(-L // split)))
+        assert torch.isnan(pm[b, ..., live:]).all() and not torch.isnan(pm[b, ..., :live]).any()
+
+
+def test_decode_merged_ragged_against_the_oracle():
+    """Every row of a ragged batch with most chunks past the ends (lengths 0,
+    shorter than q_len, chunk edges; 40 chunks of 64 keys) against the oracle."""
+    lens, q_len, Hq, Hkv, D = [0, 2, 3, 64, 65, 257, 513, 1000, 2560], 3, 32, 4, 64
+    inp = _multi_cfg(lens, q_len, Hq, Hkv, D, seed=300, split=64, max_ctx=2560,
+                     edges={1: float("-inf"), 5: 20.0})
+    out, lse, _ = _merged_gpu(inp, 64)
+    o_ref, lse_ref, _ = oracle.decode_multi(inp["q"], inp["k_cache"], inp["v_cache"],
+                                            inp["seq_lens"], inp["sinks"])
+    assert_close(out.reshape(-1, D), o_ref, what="merged decode")
+    assert_lse_close(lse.reshape(-1), lse_ref, what="merged decode lse")
