@@ -7,30 +7,39 @@ already sit in HBM:
     64 query / 8 KV heads, head_dim 64, bf16) -- sink_attn_prefill;
   * split-KV decode of 64 requests x 8192 cached tokens (64 / 8 heads, d 64,
     HND cache, 1024-token chunks) -- sink_attn_decode_split then
-    sink_attn_merge_states.
+    sink_attn_merge_states.  Step i reads copy i % 4 of the K/V caches (4.3 GB
+    per round of copies), so that no step finds its cache in the 256 MiB
+    Infinity Cache.
 All three kernels run back to back on torch's current stream; each launch is
-bracketed by HIP events on that stream.
+bracketed by HIP events on that stream.  Before the warm-up steps the step
+runs for at least --settle-ms of wall time (the shader clock takes some tens
+of milliseconds of load to settle); `settle_ms` reports it.
 
 Printed: ONE JSON line.  `value` is prefill TFLOP/s (algorithmic flops: 4*D
 per visible causal (query, key) pair, i.e. 4*D*Hq*N(N+1)/2) over the prefill
 kernel's mean event-timed duration; the `decode` object carries the decode
 KV-read GB/s (K and V of every cached token read once per KV head) over the
-split + merge duration.  `roofline` compares the prefill kernel with the
-bf16 dense MFMA peak, `decode.roofline` the decode split kernel with the HBM
-peak.  `cpu_baseline` times the fp64 CPU oracle on a bounded random sample
-of prefill rows on this host, scaled to TFLOP/s.
+split + merge duration, which `decode.roofline` compares with the HBM peak
+(the split kernel alone beside it).  `roofline` compares the prefill kernel
+with the bf16 dense MFMA peak.
 
 After the timed steps (not part of them): `hbm_read_reference` times a plain
 streaming-read kernel (libhbmprobe.so) and `decode.frac_of_measured_read`
 relates the decode to it; `extra` holds the other workloads' lines -- the
 head_dim 128 varlen prefill, chunked prefill, multi-token decode, decode over
 FP8 caches and over 16-token pages, KV-cache append, the ragged
-long-context decode at B = 1, 8, 32, 128 (B < 32 is latency bound and
-flagged so) and the one-launch decode (sink_attn_decode_fused) beside split +
-merge; the ragged, one-launch and append lines take device time from HIP-graph
-replay and cycle through copies of their inputs so that each call reads from
-HBM rather than from the 256 MiB Infinity Cache (every other line streams at
-least 512 MiB per call).
+long-context decode at B = 1, 8, 32, 128 (with the library's split size;
+B < 32 is latency bound and flagged so) and the one-launch decode
+(sink_attn_decode_fused) beside split + merge; the ragged, one-launch and
+append lines take device time from HIP-graph replay and cycle through copies
+of their inputs so that each round of calls touches at least 4 GiB.
+
+Last, the oracle leg (`cpu_baseline`, `parity`): the fp64 CPU oracle runs
+every configuration's rows on this host's cores -- the tiny and the
+GPT-OSS-shaped prefill, the split-KV decode, the ragged decode at each batch
+size and the wide-GQA varlen prefill -- timed per configuration
+(`cpu_baseline.per_config`, with the thread count and the CPU model), and the
+same rows are the all-row parity check of the GPU outputs the bench produced.
 """
 from __future__ import annotations
 
@@ -38,6 +47,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -55,6 +65,11 @@ from gqa_attention_sinks_prefill_amd import workloads as wl  # noqa: E402
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def log(msg: str) -> None:
+    """One progress line on stderr per finished phase (the JSON line alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -80,46 +95,103 @@ def measured_traffic(kernel: str):
     return None if ent is None else ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(pre_inp, cfg, out_gpu, seconds: float, seed: int = 0):
-    """Time the fp64 oracle on the prefill workload's rows, in a seeded random
-    order and in chunks, until every row is done or `seconds` have passed; the
-    same rows are the parity check of the timed GPU output."""
-    import oracle   # test infrastructure: only this leg of the benchmark uses it
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for ln in out.splitlines():
+            if ln.startswith("Model name:"):
+                return ln.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+BOUND = {"bound_max_abs": 2e-2, "bound_mean_abs": 2e-3, "bound_lse_abs": 4e-3}
+
+
+def oracle_prefill_leg(inp, cfg, out_gpu, lse_gpu, seconds: float, seed: int = 0):
+    """Time the fp64 oracle on a prefill workload's (token, head) rows, in a
+    seeded random order and in chunks, until every row is done or `seconds`
+    have passed; the same rows are the parity check of the GPU output."""
+    import oracle   # test infrastructure: only the oracle leg of the benchmark uses it
 
     threads = oracle.default_threads()
-    T, Hq, D = pre_inp["q"].shape
+    T, Hq, D = inp["q"].shape
+    cu = inp["cu_seqlens"].numpy().astype(np.int64)
     order = np.random.default_rng(seed).permutation(T * Hq)
     rows_all = np.stack([order // Hq, order % Hq], 1)
     chunk = 16384
     flops, elapsed, done = 0.0, 0.0, 0
-    max_err, sum_err = 0.0, 0.0
-    out_cpu = out_gpu.detach().cpu()
+    max_err, sum_err, lse_err = 0.0, 0.0, 0.0
+    out_cpu, lse_cpu = out_gpu.detach().cpu(), lse_gpu.detach().cpu()
     while done < len(rows_all) and elapsed < seconds:
         rows = rows_all[done:done + chunk]
         t0 = time.perf_counter()
-        o, _, _ = oracle.prefill(pre_inp["q"], pre_inp["k"], pre_inp["v"], pre_inp["sinks"],
-                                 pre_inp["cu_seqlens"], causal=True, scale=cfg.scale,
-                                 rows=rows, threads=threads)
+        o, lse, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"],
+                                   inp["cu_seqlens"], causal=True, scale=cfg.scale,
+                                   rows=rows, threads=threads)
         elapsed += time.perf_counter() - t0
-        flops += float(np.sum(4.0 * D * (rows[:, 0] + 1)))      # one sequence: pos = token
-        got = out_cpu[torch.from_numpy(rows[:, 0]), torch.from_numpy(rows[:, 1])]
-        err = np.abs(got.double().numpy() - o)
+        pos = rows[:, 0] - cu[np.searchsorted(cu, rows[:, 0], side="right") - 1]
+        flops += float(np.sum(4.0 * D * (pos + 1)))
+        t, h = torch.from_numpy(rows[:, 0]), torch.from_numpy(rows[:, 1])
+        err = np.abs(out_cpu[t, h].double().numpy() - o)
         max_err = max(max_err, float(err.max()))
         sum_err += float(err.sum())
+        fin = np.isfinite(lse)
+        lse_err = max(lse_err, float(np.abs(lse_cpu[t, h].double().numpy()[fin] - lse[fin]).max(initial=0.0)))
         done += len(rows)
     full = done == len(rows_all)
     what = ("all" if full else f"{done} random") + f" of the {len(rows_all)} (token, head) rows"
-    return ({"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads,
-             "kind": "oracle",
-             "sample": f"{what} of the 8192-token GPT-OSS-shaped prefill, {flops:.3g} "
-                       f"algorithmic flop in {elapsed:.1f} s, fp64 C + OpenMP"},
-            {"rows": int(done), "all_rows": bool(full), "max_abs": max_err,
-             "mean_abs": sum_err / (done * D), "bound_max_abs": 2e-2, "bound_mean_abs": 2e-3})
+    base = {"workload": cfg.name, "value": flops / elapsed / 1e12, "unit": "TFLOP/s",
+            "cores": threads, "seconds": round(elapsed, 2),
+            "sample": f"{what}, {flops:.3g} algorithmic flop in {elapsed:.1f} s, fp64 C + OpenMP"}
+    parity = {"workload": cfg.name, "rows": int(done), "all_rows": bool(full), "max_abs": max_err,
+              "mean_abs": sum_err / (done * D), "lse_max_abs": lse_err, **BOUND}
+    parity["ok"] = bool(max_err <= 2e-2 and parity["mean_abs"] <= 2e-3 and lse_err <= 4e-3)
+    return base, parity
 
 
-def varlen_prefill_measurement(dev, stream, reps: int):
+def oracle_decode_leg(cpu_inp, name, out_gpu, lse_gpu, kv_bytes: float):
+    """The fp64 oracle over every (request, head) row of a decode workload,
+    timed (KV GB/s of the same algorithmic bytes as the GPU line), and the
+    all-row parity check of the GPU output and lse."""
+    import oracle   # test infrastructure: only the oracle leg of the benchmark uses it
+
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    o, lse, _ = oracle.decode(cpu_inp["q"], cpu_inp["k_cache"], cpu_inp["v_cache"],
+                              cpu_inp["seq_lens"], cpu_inp["sinks"], threads=threads)
+    elapsed = time.perf_counter() - t0
+    D = o.shape[1]
+    got = out_gpu.detach().cpu().double().numpy().reshape(-1, D)
+    err = np.abs(got - o)
+    g_lse = lse_gpu.detach().cpu().double().numpy().reshape(-1)
+    fin = np.isfinite(lse)
+    lse_err = float(np.abs(g_lse[fin] - lse[fin]).max(initial=0.0))
+    base = {"workload": name, "value": kv_bytes / elapsed / 1e9, "unit": "GB/s",
+            "cores": threads, "seconds": round(elapsed, 2),
+            "sample": f"all {o.shape[0]} (request, head) rows, fp64 C + OpenMP"}
+    parity = {"workload": name, "rows": int(o.shape[0]), "all_rows": True,
+              "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+              "lse_max_abs": lse_err, **BOUND}
+    parity["ok"] = bool(parity["max_abs"] <= 2e-2 and parity["mean_abs"] <= 2e-3
+                        and lse_err <= 4e-3 and np.array_equal(np.isneginf(g_lse), np.isneginf(lse)))
+    return base, parity
+
+
+def varlen_prefill_measurement(dev, stream, reps: int, keep: dict | None = None):
     """TFLOP/s of the wide-GQA varlen prefill (16 packed sequences of U[512, 6000]
-    tokens, 64 q / 4 KV heads, head_dim 128, causal), event-timed like the main line."""
+    tokens, 64 q / 4 KV heads, head_dim 128, causal), event-timed like the main
+    line.  With `keep`, one more call (with lse) leaves its inputs and outputs
+    there for the oracle leg."""
     cfg = wl.VARLEN_PREFILL
     inp = wl.prefill_inputs(cfg)
     q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
@@ -127,8 +199,8 @@ def varlen_prefill_measurement(dev, stream, reps: int):
     out = torch.empty_like(q)
     run = lambda: sa.sink_attn_prefill(q, k, v, sinks, cu, inp["max_seqlen"], causal=True,
                                        scale=cfg.scale, out=out, stream=stream)
-    run()
-    run()
+    for _ in range(3):
+        run()
     torch.cuda.synchronize()
     e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
          for _ in range(reps)]
@@ -140,6 +212,13 @@ def varlen_prefill_measurement(dev, stream, reps: int):
     ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
     flops = wl.prefill_flops(inp["seqlens"].tolist(), cfg.num_q_heads, cfg.head_dim)
     tf = flops / (ms * 1e-3) / 1e12
+    if keep is not None:
+        out.fill_(float("nan"))
+        lse = torch.full((q.shape[0], q.shape[1]), float("nan"), device=dev)
+        sa.sink_attn_prefill(q, k, v, sinks, cu, inp["max_seqlen"], causal=True,
+                             scale=cfg.scale, out=out, lse=lse, stream=stream)
+        torch.cuda.synchronize()
+        keep.update(inp=inp, cfg=cfg, out=out.cpu(), lse=lse.cpu())
     return {"workload": cfg.name, "value": round(tf, 2), "unit": "TFLOP/s",
             "mean_launch_ms": round(ms, 4), "algorithmic_flop_per_launch": flops,
             "roofline": {"bound": "mfma", "peak": round(PEAK_BF16_TFLOPS, 1),
@@ -369,11 +448,15 @@ def hbm_read_reference(dev, stream, reps: int = 10):
             "bytes": nbytes, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s"}
 
 
-def rotation(touched_bytes: float) -> int:
+ROTATE_BYTES = 4 << 30
+
+
+def rotation(touched_bytes: float, target: int = ROTATE_BYTES) -> int:
     """Copies of a call's inputs to cycle through so that one round of them
-    touches >= 1 GiB: a timed call then finds its bytes in HBM, not left in
-    the 256 MiB Infinity Cache by the call before."""
-    return int(min(32, max(1, -(-(1 << 30) // max(int(touched_bytes), 1)))))
+    touches >= `target` bytes (4 GiB, 16x the 256 MiB Infinity Cache): a timed
+    call then finds its bytes in HBM, not left in that cache by the calls
+    before it.  At most 20, the calls one timed graph holds."""
+    return int(min(20, max(1, -(-int(target) // max(int(touched_bytes), 1)))))
 
 
 def graph_ms(run, stream, calls: int = 20, reps: int = 10) -> float:
@@ -408,69 +491,95 @@ def graph_ms(run, stream, calls: int = 20, reps: int = 10) -> float:
     return float(np.mean([a.elapsed_time(b) for a, b in e])) / calls
 
 
-def _decode_buffers(cfg, dev):
+def _decode_buffers(cfg, dev, split=None):
     """Inputs of a decode workload on the GPU, with `rotation` copies of the
-    caches when one call touches less than 1 GiB."""
+    caches, partials for chunks of `split` tokens (the config's by default),
+    and the CPU inputs (for the oracle leg)."""
     d = wl.decode_inputs(cfg)
     q, kc, vc = d["q"].to(dev), d["k_cache"].to(dev), d["v_cache"].to(dev)
     B, Hq, D = q.shape
-    ns = cfg.num_splits
+    split = cfg.split_size if split is None else split
+    ns = -(-cfg.max_ctx // split)
     kv = wl.decode_kv_bytes(d["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
     n = rotation(kv)
     caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(n - 1)]
     return dict(q=q, caches=caches, lens=d["seq_lens"].to(dev), sinks=d["sinks"].to(dev), ns=ns,
+                split=split,
                 part=(torch.empty(B, Hq, ns, D, device=dev), torch.empty(B, Hq, ns, device=dev),
                       torch.empty(B, Hq, ns, device=dev)),
                 out=torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev),
-                counters=sa.decode_counters(B, Hq, kc.shape[1], 1, dev), kv=kv)
+                lse=torch.empty(B, Hq, device=dev),
+                counters=sa.decode_counters(B, Hq, kc.shape[1], 1, dev), kv=kv, cpu=d)
 
 
 def _split_merge(cfg, x):
     def run(s, i):
         kc, vc = x["caches"][i % len(x["caches"])]
-        sa.sink_attn_decode(x["q"], kc, vc, x["lens"], x["sinks"], cfg.split_size, x["ns"],
+        sa.sink_attn_decode(x["q"], kc, vc, x["lens"], x["sinks"], x["split"], x["ns"],
                             scale=cfg.scale, out=x["out"], partials=x["part"], stream=s)
     return run
 
 
-def _merged(cfg, x):
+def _merged(cfg, x, lse=False):
     def run(s, i):
         kc, vc = x["caches"][i % len(x["caches"])]
-        sa.sink_attn_decode_merged(x["q"], kc, vc, x["lens"], x["sinks"], cfg.split_size, x["ns"],
-                                   scale=cfg.scale, out=x["out"], partials=x["part"], stream=s)
+        sa.sink_attn_decode_merged(x["q"], kc, vc, x["lens"], x["sinks"], x["split"], x["ns"],
+                                   scale=cfg.scale, out=x["out"], partials=x["part"],
+                                   lse=x["lse"] if lse else None, stream=s)
     return run
 
 
 def _one_launch(cfg, x):
     def run(s, i):
         kc, vc = x["caches"][i % len(x["caches"])]
-        sa.sink_attn_decode_fused(x["q"], kc, vc, x["lens"], x["sinks"], cfg.split_size,
+        sa.sink_attn_decode_fused(x["q"], kc, vc, x["lens"], x["sinks"], x["split"],
                                   x["ns"], scale=cfg.scale, counters=x["counters"],
                                   out=x["out"], partials=x["part"], stream=s)
     return run
 
 
-def ragged_decode_measurement(dev, stream, batch: int, reps: int):
-    """KV GB/s of split decode + merge over contexts U[1024, 32768] (64 / 8 heads,
-    d 64, 1024-token chunks), device time from graph replay; B = 1 and 8 are
-    latency bound.  The value is sink_attn_decode_merged (chunks past a
-    request's end write no state; the merge stops at the last chunk with
-    keys); split decode + sink_attn_merge_states is timed beside it."""
+def ragged_decode_measurement(dev, stream, batch: int, reps: int, keep: dict | None = None):
+    """KV GB/s of ragged decode over contexts U[1024, 32768] (64 / 8 heads, d 64)
+    through sink_attn_decode_merged (chunks past a request's end write no
+    state; the merge stops at the last chunk with keys), with the chunk size
+    sink_attn_decode_split_size picks for the shape; device time from graph
+    replay.  Beside it: the same call with 1024-token chunks, and split decode
+    + sink_attn_merge_states.  B = 1 and 8 are latency bound.  With `keep`,
+    one more call (with lse) leaves the CPU inputs and the outputs there for
+    the oracle leg."""
     cfg = wl.ragged_decode(batch)
-    x = _decode_buffers(cfg, dev)
+    split = sa.sink_attn_decode_split_size(batch, cfg.max_ctx, cfg.num_q_heads,
+                                           cfg.num_kv_heads, cfg.head_dim)
+    x = _decode_buffers(cfg, dev, split)
     reps = max(3, reps // 2)
     two = graph_ms(_split_merge(cfg, x), stream, reps=reps)
     ms = graph_ms(_merged(cfg, x), stream, reps=reps)
-    gbs = x["kv"] / (ms * 1e-3) / 1e9
+    line = {"workload": cfg.name, "unit": "GB/s",
+            "metric": "decode KV GB/s (split + length-aware merge, graph replay)",
+            "split_size": split, "mean_ms": round(ms, 4), "split_merge_ms_same_run": round(two, 4)}
+    if split != cfg.split_size:
+        B, Hq, D = x["q"].shape
+        ns1 = cfg.num_splits
+        x1024 = dict(x, split=cfg.split_size, ns=ns1,
+                     part=(torch.empty(B, Hq, ns1, D, device=dev), torch.empty(B, Hq, ns1, device=dev),
+                           torch.empty(B, Hq, ns1, device=dev)))
+        line["split1024_ms_same_run"] = round(graph_ms(_merged(cfg, x1024), stream, reps=reps), 4)
+        del x1024
     kv = x["kv"]
+    gbs = kv / (ms * 1e-3) / 1e9
+    line.update({"value": round(gbs, 1), "algorithmic_bytes_per_step": kv,
+                 "cache_copies_rotated": len(x["caches"]), "latency_bound": batch < 32,
+                 "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS,
+                              "frac": round(gbs / PEAK_HBM_GBS, 4)}})
+    if keep is not None:
+        x["out"].fill_(float("nan"))
+        x["lse"].fill_(float("nan"))
+        _merged(cfg, x, lse=True)(stream, 0)
+        torch.cuda.synchronize()
+        keep.update(cpu=x["cpu"], name=cfg.name, out=x["out"].cpu(), lse=x["lse"].cpu(), kv=kv)
     del x
     torch.cuda.empty_cache()
-    return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
-            "metric": "decode KV GB/s (split + length-aware merge, graph replay)",
-            "mean_ms": round(ms, 4), "split_merge_ms_same_run": round(two, 4),
-            "algorithmic_bytes_per_step": kv, "cache_copies_rotated": rotation(kv),
-            "latency_bound": batch < 32,
-            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    return line
 
 
 def one_launch_decode_measurement(dev, stream, cfg, reps: int):
@@ -510,10 +619,13 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=30,
-                    help="untimed steps first; the clocks take some 20 ms of load to settle")
-    ap.add_argument("--cpu-seconds", type=float, default=45.0,
-                    help="host time budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--warmup", type=int, default=30, help="untimed steps before the timed ones")
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="wall time of untimed steps run before the warm-up steps, whatever "
+                         "--warmup says (the shader clock settles under some tens of ms of load)")
+    ap.add_argument("--cpu-seconds", type=float, default=150.0,
+                    help="host time budget of the oracle per prefill workload (0 disables the "
+                         "oracle leg)")
     ap.add_argument("--only", choices=("all", "prefill", "decode", "varlen", "ragged", "mtp",
                                        "fp8", "read"),
                     default="all",
@@ -522,7 +634,7 @@ def main():
                          "FP8-cache decode / the streaming-read reference (for hardware-counter "
                          "runs)")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the extra wide-GQA varlen (head_dim 128) prefill measurement")
+                    help="skip the extra workloads' lines (and their oracle checks)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device-to-device copy instead (scales HBM counters)")
     args = ap.parse_args()
@@ -561,6 +673,9 @@ def main():
     out = torch.empty_like(q)
     dq, kc, vc = dec["q"].to(dev), dec["k_cache"].to(dev), dec["v_cache"].to(dev)
     lens, sinks_d = dec["seq_lens"].to(dev), dec["sinks"].to(dev)
+    kv_bytes = wl.decode_kv_bytes(dec["seq_lens"].tolist(), dcfg.num_kv_heads, dcfg.head_dim)
+    # copies of the caches, cycled through step by step (>= 4 GiB per round)
+    caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(rotation(kv_bytes) - 1)]
     B, Hq, D = dq.shape
     ns = -(-kc.shape[2] // dcfg.split_size)
     po = torch.empty(B, Hq, ns, D, device=dev)
@@ -568,18 +683,20 @@ def main():
     pd = torch.empty(B, Hq, ns, device=dev)
     dout = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
+    log("inputs resident in HBM")
 
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
-    def step(e=None):
+    def step(i, e=None, copy=None):
+        kc_i, vc_i = caches[i % len(caches) if copy is None else copy]
         if e: e[0].record(stream)
         if run_p:
             sa.sink_attn_prefill(q, k, v, sinks_p, cu, pre["max_seqlen"], causal=True,
                                  scale=pcfg.scale, out=out, stream=stream)
         if e: e[1].record(stream)
         if run_d:
-            sa.sink_attn_decode_split(dq, kc, vc, lens, sinks_d, dcfg.split_size, ns,
+            sa.sink_attn_decode_split(dq, kc_i, vc_i, lens, sinks_d, dcfg.split_size, ns,
                                       scale=dcfg.scale, part_o=po, part_m=pm, part_d=pd,
                                       stream=stream)
         if e: e[2].record(stream)
@@ -587,23 +704,48 @@ def main():
             sa.sink_attn_merge_states(po, pm, pd, out=dout, stream=stream)
         if e: e[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    # ---- settle (wall-time bound), warm-up, timed steps ---------------------------
+    t_settle, n_settle = time.perf_counter(), 0
+    while True:
+        step(n_settle)
+        n_settle += 1
+        if n_settle % 8 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t_settle) * 1e3 >= args.settle_ms:
+                break
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
+    log(f"settled: {n_settle} steps in {settle_ms:.0f} ms")
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev[i])
+        step(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    log(f"{args.steps} timed steps done")
 
     pre_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     split_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     merge_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
     flops = wl.prefill_flops(pre["seqlens"].tolist(), pcfg.num_q_heads, pcfg.head_dim)
-    kv_bytes = wl.decode_kv_bytes(dec["seq_lens"].tolist(), dcfg.num_kv_heads, dcfg.head_dim)
     tflops = flops / (pre_ms * 1e-3) / 1e12
     dec_gbs = kv_bytes / ((split_ms + merge_ms) * 1e-3) / 1e9
     split_gbs = kv_bytes / (split_ms * 1e-3) / 1e9
+
+    # the decode with one cache copy read over and over (for comparison only)
+    single = None
+    if run_d:
+        es = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+              for _ in range(max(5, args.steps))]
+        for i, e in enumerate(es):
+            step(i, e, copy=0)
+        torch.cuda.synchronize()
+        one_ms = float(np.mean([e[1].elapsed_time(e[3]) for e in es]))
+        single = {"ms": round(one_ms, 4), "value": round(kv_bytes / (one_ms * 1e-3) / 1e9, 1),
+                  "unit": "GB/s",
+                  "note": "split + merge re-reading one 1.07 GB cache copy every step "
+                          "(part of it can stay in the Infinity Cache); not the reported value"}
 
     traffic_p = measured_traffic("prefill")
     traffic_d = measured_traffic("decode_split")
@@ -614,6 +756,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": round(settle_ms, 1),
+        "settle_steps": n_settle,
         "ms_per_step": round(wall / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -623,47 +767,109 @@ def main():
         "config": {"workload": pcfg.name, "decode_workload": dcfg.name,
                    "seq_len": 8192, "num_q_heads": 64, "num_kv_heads": 8, "head_dim": 64,
                    "causal": True, "decode_batch": dcfg.batch, "decode_ctx": dcfg.ctx,
-                   "decode_split_size": dcfg.split_size, "parallelism": "none (1 GPU)"},
+                   "decode_split_size": dcfg.split_size,
+                   "decode_cache_copies_rotated": len(caches), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
                      "peak": round(PEAK_BF16_TFLOPS, 1), "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_p, "kernel": "prefill_kernel<64,4,2>",
                      "algorithmic_flop_per_launch": flops, "mean_launch_ms": round(pre_ms, 4)},
-        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "metric": "decode KV GB/s",
+        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s",
+                   "metric": "decode KV GB/s (split + merge)",
                    "ms": round(split_ms + merge_ms, 4), "split_ms": round(split_ms, 4),
                    "merge_ms": round(merge_ms, 4),
-                   "roofline": {"bound": "hbm", "achieved": round(split_gbs, 1),
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1),
                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": round(split_gbs / PEAK_HBM_GBS, 4),
-                                "traffic": traffic_d, "kernel": "decode_split_kernel<64,1,4,false,false>",
-                                "algorithmic_bytes_per_launch": kv_bytes},
-                   "frac_of_hbm_peak_incl_merge": round(dec_gbs / PEAK_HBM_GBS, 4)},
+                                "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                                "kernels": "decode_split_kernel<64,1,4,false,false> + "
+                                           "merge_rows_kernel<64>",
+                                "algorithmic_bytes_per_step": kv_bytes,
+                                "split_only": {"achieved": round(split_gbs, 1),
+                                               "frac": round(split_gbs / PEAK_HBM_GBS, 4),
+                                               "traffic": traffic_d}},
+                   "single_cache_copy": single},
         "device": {"name": props.name, "compute_units": props.multi_processor_count,
                    "gcn_arch": getattr(props, "gcnArchName", "")},
     }
+    oracle_on = args.cpu_seconds > 0
+    keep_varlen = {} if oracle_on else None
+    keep_ragged = {b: ({} if oracle_on else None) for b in wl.RAGGED_BATCHES}
     if run_p and not args.no_extra:
-        res["extra"] = [varlen_prefill_measurement(dev, stream, max(3, args.steps // 2)),
-                        chunked_prefill_measurement(dev, stream, max(3, args.steps // 2)),
-                        multi_decode_measurement(dev, stream, max(3, args.steps // 2)),
-                        fp8_decode_measurement(dev, stream, max(3, args.steps // 2)),
-                        paged_decode_measurement(dev, stream, max(3, args.steps // 2)),
-                        kv_append_measurement(dev, stream, max(3, args.steps // 2))]
-        res["extra"] += [ragged_decode_measurement(dev, stream, b, max(3, args.steps // 4))
-                         for b in wl.RAGGED_BATCHES]
-        res["extra"] += [one_launch_decode_measurement(dev, stream, c, max(3, args.steps // 4))
-                         for c in (wl.SPLIT_DECODE, wl.ragged_decode(1), wl.ragged_decode(128))]
+        r2, r4 = max(3, args.steps // 2), max(3, args.steps // 4)
+        jobs = [lambda: varlen_prefill_measurement(dev, stream, r2, keep=keep_varlen),
+                lambda: chunked_prefill_measurement(dev, stream, r2),
+                lambda: multi_decode_measurement(dev, stream, r2),
+                lambda: fp8_decode_measurement(dev, stream, r2),
+                lambda: paged_decode_measurement(dev, stream, r2),
+                lambda: kv_append_measurement(dev, stream, r2)]
+        jobs += [lambda b=b: ragged_decode_measurement(dev, stream, b, r4, keep=keep_ragged[b])
+                 for b in wl.RAGGED_BATCHES]
+        jobs += [lambda c=c: one_launch_decode_measurement(dev, stream, c, r4)
+                 for c in (wl.SPLIT_DECODE, wl.ragged_decode(1), wl.ragged_decode(128))]
+        res["extra"] = []
+        for job in jobs:
+            res["extra"].append(job())
+            log(f"extra line {res['extra'][-1]['workload']} done")
     if run_d and not args.no_extra:
         ref = hbm_read_reference(dev, stream)
         res["hbm_read_reference"] = ref
-        res["decode"]["frac_of_measured_read"] = round(split_gbs / ref["value"], 4)
+        res["decode"]["frac_of_measured_read"] = round(dec_gbs / ref["value"], 4)
+        res["decode"]["roofline"]["split_only"]["frac_of_measured_read"] = round(
+            split_gbs / ref["value"], 4)
     if args.only != "all":
         res["note"] = f"--only {args.only}: the other part of the step was not launched"
-    if args.cpu_seconds > 0 and run_p:
-        cb, parity = cpu_baseline(pre, pcfg, out, args.cpu_seconds)
-        res["cpu_baseline"] = cb
-        res["parity_spot_check"] = parity
-    else:
-        res["cpu_baseline"] = None
+
+    # ---- oracle leg: CPU baseline per workload and all-row parity --------------
+    res["cpu_baseline"] = None
+    if oracle_on and run_p:
+        import oracle   # test infrastructure: only this leg of the benchmark uses it
+        per, parity = [], []
+        lse = torch.empty(out.shape[0], out.shape[1], device=dev)
+        sa.sink_attn_prefill(q, k, v, sinks_p, cu, pre["max_seqlen"], causal=True,
+                             scale=pcfg.scale, out=out, lse=lse, stream=stream)
+        torch.cuda.synchronize()
+        b, p = oracle_prefill_leg(pre, pcfg, out, lse, args.cpu_seconds)
+        per.append(b)
+        parity.append(p)
+        log(f"oracle {pcfg.name}: {b['seconds']} s")
+        tiny = wl.prefill_inputs(wl.TINY_PREFILL)
+        t_out = torch.empty(tiny["q"].shape, dtype=torch.bfloat16, device=dev)
+        t_lse = torch.empty(tiny["q"].shape[:2], device=dev)
+        sa.sink_attn_prefill(tiny["q"].to(dev), tiny["k"].to(dev), tiny["v"].to(dev),
+                             tiny["sinks"].to(dev), tiny["cu_seqlens"].to(dev),
+                             tiny["max_seqlen"], causal=True, scale=wl.TINY_PREFILL.scale,
+                             out=t_out, lse=t_lse, stream=stream)
+        torch.cuda.synchronize()
+        b, p = oracle_prefill_leg(tiny, wl.TINY_PREFILL, t_out, t_lse, args.cpu_seconds)
+        per.append(b)
+        parity.append(p)
+        if run_d:
+            d_lse = torch.empty(B, Hq, device=dev)
+            sa.sink_attn_merge_states(po, pm, pd, out=dout, lse=d_lse, stream=stream)
+            torch.cuda.synchronize()
+            b, p = oracle_decode_leg(dec, dcfg.name, dout, d_lse, kv_bytes)
+            per.append(b)
+            parity.append(p)
+            log(f"oracle {dcfg.name}: {b['seconds']} s")
+        for kr in keep_ragged.values():
+            if kr:
+                b, p = oracle_decode_leg(kr["cpu"], kr["name"], kr["out"], kr["lse"], kr["kv"])
+                per.append(b)
+                parity.append(p)
+                log(f"oracle {kr['name']}: {b['seconds']} s")
+                kr.clear()
+        if keep_varlen:
+            b, p = oracle_prefill_leg(keep_varlen["inp"], keep_varlen["cfg"], keep_varlen["out"],
+                                      keep_varlen["lse"], args.cpu_seconds)
+            per.append(b)
+            parity.append(p)
+            log(f"oracle {keep_varlen['cfg'].name}: {b['seconds']} s")
+        head = dict(per[0])
+        res["cpu_baseline"] = {"value": head["value"], "unit": head["unit"], "cores": head["cores"],
+                               "kind": "oracle", "cpu_model": cpu_model(),
+                               "sample": head["sample"] + f" ({pcfg.name})",
+                               "per_config": per}
+        res["parity"] = {"all_ok": all(p["ok"] for p in parity), "per_config": parity}
     print(json.dumps(res), flush=True)
 
 

@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
                sink_attn_decode_fused (split and merge in one launch; counters from
                decode_counters), sink_attn_decode_merged (split and a merge over
                the chunks that hold keys; for ragged batches)
+               sink_attn_decode_split_size (the library's chunk size for a shape)
   KV cache     sink_attn_kv_append, sink_attn_kv_append_fp8, sink_attn_kv_append_paged
 and the wrappers sink_attn_decode, sink_attn_decode_multi, sink_attn_decode_fp8 and
 sink_attn_decode_paged (split + merge on one stream).
@@ -33,6 +34,7 @@ __all__ = ["sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_s
            "sink_attn_kv_append", "sink_attn_decode_multi_split_fp8", "sink_attn_decode_fp8",
            "sink_attn_kv_append_fp8", "sink_attn_decode_paged_split", "sink_attn_decode_paged",
            "sink_attn_kv_append_paged", "sink_attn_decode_fused", "sink_attn_decode_merged", "decode_counters",
+           "sink_attn_decode_split_size",
            "SinkAttnError", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +45,8 @@ EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn
                     "sink_attn_decode_multi_split_fp8", "sink_attn_decode_paged_split",
                     "sink_attn_decode_fused", "sink_attn_decode_merged",
                     "sink_attn_merge_states", "sink_attn_kv_append", "sink_attn_kv_append_fp8",
-                    "sink_attn_kv_append_paged", "sink_attn_last_error")
+                    "sink_attn_kv_append_paged", "sink_attn_decode_split_size",
+                    "sink_attn_last_error")
 
 
 class SinkAttnError(RuntimeError):
@@ -110,6 +113,8 @@ def load_library():
     fused = list(lib.sink_attn_decode_fused.argtypes)
     lib.sink_attn_decode_merged.argtypes = fused[:25] + fused[26:]
     lib.sink_attn_decode_merged.restype = ctypes.c_int
+    lib.sink_attn_decode_split_size.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.sink_attn_decode_split_size.restype = ctypes.c_int32
     lib.sink_attn_last_error.argtypes = []
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -634,6 +639,17 @@ def sink_attn_kv_append_paged(k_new, v_new, cu_seqlens_new, cache_pos, k_pages, 
     return k_pages, v_pages
 
 
+def sink_attn_decode_split_size(batch, max_ctx, num_q_heads, num_kv_heads, head_dim, q_len=1):
+    """Tokens per chunk for split-KV decode of this launch shape (the library's
+    choice: 1024, or 2048 when that still gives every SIMD four work units)."""
+    rc = load_library().sink_attn_decode_split_size(int(batch), int(max_ctx), int(q_len),
+                                                    int(num_q_heads), int(num_kv_heads),
+                                                    int(head_dim))
+    if rc <= 0:
+        _check("sink_attn_decode_split_size", rc if rc != 0 else -1)
+    return int(rc)
+
+
 # ------------------------------------------------------- one-launch decode --
 def decode_counters(batch, num_q_heads, num_kv_heads, q_len=1, device="cuda"):
     """Zeroed arrival counters for sink_attn_decode_fused, sized for the shape
@@ -767,3 +783,4 @@ def sink_attn_decode_merged(q, k_cache, v_cache, seq_lens, sinks, split_size, nu
         _stream(stream))
     _check("sink_attn_decode_merged", rc)
     return out
+

@@ -390,6 +390,25 @@ int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_h
                                       split_size, num_splits, part_o, part_m, part_d, stream);
 }
 
+int32_t sink_attn_decode_split_size(int32_t batch, int32_t max_ctx, int32_t q_len,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  g_err[0] = '\0';
+  if (batch < 0 || max_ctx < 0) return fail(SINK_ATTN_EINVAL, "batch and max_ctx must be >= 0");
+  if (q_len < 1) return fail(SINK_ATTN_EINVAL, "q_len must be >= 1 (got %d)", q_len);
+  if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
+  int device = 0, cus = 0;
+  if (hipGetDevice(&device) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  const int64_t ncols = static_cast<int64_t>(q_len) * (num_q_heads / num_kv_heads);
+  const int cols_per_block = 16 * sinkattn::decode_column_blocks(
+      static_cast<int>(ncols > 0x7fffffff ? 0x7fffffff : ncols), head_dim);
+  const int64_t slices = (ncols + cols_per_block - 1) / cols_per_block;
+  return sinkattn::decode_split_size(static_cast<int64_t>(batch) * num_kv_heads * slices, max_ctx,
+                                     head_dim, cus);
+}
+
 int sink_attn_merge_states(const float* part_o, const float* part_m, const float* part_d,
                            int32_t batch, int32_t num_q_heads, int32_t num_splits,
                            int32_t head_dim, void* o, int64_t o_stride_b,

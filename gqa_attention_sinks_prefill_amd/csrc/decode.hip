@@ -850,6 +850,21 @@ int decode_waves_per_unit(int64_t num_units, int head_dim, int column_blocks) {
   return num_units >= simds ? 1 : (2 * num_units >= simds ? 2 : 4);
 }
 
+int decode_split_size(int64_t column_units, int max_ctx, int head_dim, int cus) {
+  // 1024-token chunks, or 2048 when even those give every SIMD four units at
+  // the longest context.  Measured (ragged contexts U[1024, 32768], d 64,
+  // length-aware split + merge, graph replay): B = 128 / 32 ran 748 / 188 us
+  // with 2048 against 788 / 191 with 1024 (fewer chunk states, longer runs of
+  // one head per wave); B = 8 / 1 ran 69 / 25 us with 2048 against 59 / 17
+  // with 1024, and smaller chunks were slower at every batch size (B = 1:
+  // 19 us at 512, 24 at 256), the per-unit work (query load, state write,
+  // merge input) outweighing the extra parallelism.
+  (void)head_dim;
+  const int64_t simds = (int64_t)cus * 4;
+  const int64_t units_2048 = column_units * ((max_ctx + 2047) / 2048);
+  return units_2048 >= 4 * simds ? 2048 : 1024;
+}
+
 template <int D, int CB, bool F8, bool PG>
 hipError_t launch_decode_cb(const DecodeArgs& a, int64_t num_units, int waves, hipStream_t stream) {
   const dim3 grid((unsigned)num_units);

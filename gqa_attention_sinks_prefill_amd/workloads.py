@@ -105,12 +105,13 @@ MTP_DECODE = DecodeConfig("mtp_decode_b64_q4_ctx8192_h64kv8_d64_split1024", 64, 
 
 
 def ragged_decode(batch: int) -> DecodeConfig:
-    """Long-context ragged decode: contexts U[1024, 32768], 64 q / 8 KV heads, d 64.
+    """Long-context ragged decode: contexts U[1024, 32768], 64 q / 8 KV heads, d 64
+    (1024-token chunks unless a caller picks another split size).
 
     Head 0 gets sink -inf (plain attention) and head 63 (another GQA group)
     gets sink +20 (the sink dominates the softmax).
     """
-    return DecodeConfig(f"ragged_decode_b{batch}_ctx1024to32768_h64kv8_d64_split1024",
+    return DecodeConfig(f"ragged_decode_b{batch}_ctx1024to32768_h64kv8_d64",
                         batch, None, (1024, 32768), 32768, 64, 8, 64, (-4.0, 4.0),
                         split_size=1024, seed=3,
                         edge_sinks={0: float("-inf"), 63: 20.0})

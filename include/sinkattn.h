@@ -191,6 +191,24 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
                                  float* part_d, void* stream);
 
 /*
+ * A chunk size for the split-KV decode calls above and below, chosen from the
+ * launch shape alone (the request lengths are device values): "GPT-OSS on day
+ * 0", section "Kernels for GPT-OSS / Sink-Attention", parallelises decode over
+ * the KV length as well as over heads.  Returns 1024 tokens, or 2048 when
+ * chunks of 2048 at the longest context (max_ctx) still give every SIMD of the
+ * current device four (request, KV head, column slice, chunk) work units:
+ * longer chunks then write fewer chunk states for the merge, while smaller
+ * batches keep the parallelism of 1024-token chunks.  Always a positive
+ * multiple of 64.  Size the partials with num_splits = ceil(max_ctx / split).
+ *   batch, max_ctx >= 0; q_len >= 1; heads and head_dim as for
+ *   sink_attn_decode_multi_split.
+ * Returns the split size, or SINK_ATTN_EINVAL / SINK_ATTN_EUNSUPPORTED (with a
+ * message) for invalid arguments.  Enqueues nothing.
+ */
+int32_t sink_attn_decode_split_size(int32_t batch, int32_t max_ctx, int32_t q_len,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
+
+/*
  * Second half of split-KV decode: merge each row's chunk states by their
  * log-sum-exp weights (the pages state that chunks are formed and that only
  * the first carries the sink; the merge is the exact recombination this

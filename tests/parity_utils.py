@@ -9,9 +9,10 @@ import torch
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
 # lse = m + ln(d).  The kernels accumulate d from the same bf16-rounded
-# weights that multiply V (relative rounding <= 2^-9 each, so the sum is off by
-# a relative <= 2^-9 too), with fp32 logits and fp32 accumulation: |dlse| <=
-# ln(1 + 2^-8) ~ 3.9e-3.
+# weights that multiply V: bf16 keeps 8 significant bits, so round-to-nearest
+# changes each weight by a relative <= 2^-8 (the unit roundoff) and a sum of
+# such weights by a relative <= 2^-8 too; with fp32 logits and fp32
+# accumulation around it, |dlse| <= ln(1 + 2^-8) ~ 3.9e-3.
 LSE_ABS = 4e-3
 
 

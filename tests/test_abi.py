@@ -483,3 +483,36 @@ def test_decode_merged_empty_batch_is_a_noop():
     rc, msg = _decode_merged(batch=0, q=None, k=None, v=None, lens=None, sinks=None, po=None,
                              pm=None, pd=None, o=None)
     assert rc == 0, msg
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(batch=-1), -1, ">= 0"),
+    (dict(max_ctx=-5), -1, ">= 0"),
+    (dict(q_len=0), -1, "q_len"),
+    (dict(hq=6, hkv=4), -1, "multiple"),
+    (dict(d=96), -2, "head_dim"),
+])
+def test_decode_split_size_rejects_bad_arguments(kw, code, needle):
+    a = dict(batch=8, max_ctx=32768, q_len=1, hq=64, hkv=8, d=64)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_decode_split_size(a["batch"], a["max_ctx"], a["q_len"], a["hq"], a["hkv"],
+                                         a["d"])
+    assert rc == code and needle in lib.sink_attn_last_error().decode()
+
+
+def test_decode_split_size_follows_the_launch_shape():
+    # host only: no device work is enqueued (without a GPU the CU count
+    # falls back to the MI355X's 256)
+    for batch in (0, 1, 2, 8, 64, 1024):
+        for max_ctx in (0, 1, 1000, 8192, 32768, 1 << 20):
+            for q_len, hq, hkv, d in ((1, 64, 8, 64), (4, 64, 8, 64), (1, 64, 4, 128)):
+                s = sa.sink_attn_decode_split_size(batch, max_ctx, hq, hkv, d, q_len)
+                assert s in (1024, 2048)
+    # few or short requests keep 1024-token chunks; many long ones get 2048
+    assert sa.sink_attn_decode_split_size(64, 8192, 64, 8, 64) == 1024
+    assert sa.sink_attn_decode_split_size(1, 32768, 64, 8, 64) == 1024
+    assert sa.sink_attn_decode_split_size(8, 32768, 64, 8, 64) == 1024
+    assert sa.sink_attn_decode_split_size(32, 32768, 64, 8, 64) == 2048
+    assert sa.sink_attn_decode_split_size(128, 32768, 64, 8, 64) == 2048
+
