@@ -16,6 +16,8 @@ Entry points (same names as the C ABI):
                sink_attn_decode_fused (split and merge in one launch; counters from
                decode_counters), sink_attn_decode_merged (split and a merge over
                the chunks that hold keys; for ragged batches)
+               sink_attn_decode_merged_noalloc (the same with the chunk states in
+               the library's device scratch array: no buffers beyond in- and outputs),
                sink_attn_decode_split_size (the library's chunk size for a shape)
   KV cache     sink_attn_kv_append, sink_attn_kv_append_fp8, sink_attn_kv_append_paged
 and the wrappers sink_attn_decode, sink_attn_decode_multi, sink_attn_decode_fp8 and
@@ -34,7 +36,7 @@ __all__ = ["sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn_decode_s
            "sink_attn_kv_append", "sink_attn_decode_multi_split_fp8", "sink_attn_decode_fp8",
            "sink_attn_kv_append_fp8", "sink_attn_decode_paged_split", "sink_attn_decode_paged",
            "sink_attn_kv_append_paged", "sink_attn_decode_fused", "sink_attn_decode_merged", "decode_counters",
-           "sink_attn_decode_split_size",
+           "sink_attn_decode_split_size", "sink_attn_decode_merged_noalloc",
            "SinkAttnError", "library_path", "load_library", "EXPORTED_SYMBOLS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -46,7 +48,7 @@ EXPORTED_SYMBOLS = ("sink_attn_prefill", "sink_attn_prefill_chunked", "sink_attn
                     "sink_attn_decode_fused", "sink_attn_decode_merged",
                     "sink_attn_merge_states", "sink_attn_kv_append", "sink_attn_kv_append_fp8",
                     "sink_attn_kv_append_paged", "sink_attn_decode_split_size",
-                    "sink_attn_last_error")
+                    "sink_attn_decode_merged_noalloc", "sink_attn_last_error")
 
 
 class SinkAttnError(RuntimeError):
@@ -113,6 +115,9 @@ def load_library():
     fused = list(lib.sink_attn_decode_fused.argtypes)
     lib.sink_attn_decode_merged.argtypes = fused[:25] + fused[26:]
     lib.sink_attn_decode_merged.restype = ctypes.c_int
+    # ... and without the partial buffers either
+    lib.sink_attn_decode_merged_noalloc.argtypes = fused[:22] + fused[26:]
+    lib.sink_attn_decode_merged_noalloc.restype = ctypes.c_int
     lib.sink_attn_decode_split_size.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.sink_attn_decode_split_size.restype = ctypes.c_int32
     lib.sink_attn_last_error.argtypes = []
@@ -784,3 +789,52 @@ def sink_attn_decode_merged(q, k_cache, v_cache, seq_lens, sinks, split_size, nu
     _check("sink_attn_decode_merged", rc)
     return out
 
+
+def sink_attn_decode_merged_noalloc(q, k_cache, v_cache, seq_lens, sinks, split_size,
+                                    num_splits=None, *, k_scale=None, v_scale=None, max_ctx=None,
+                                    scale=None, out=None, lse=None, stream=None):
+    """sink_attn_decode_merged with its chunk states in the library's device
+    scratch array (128 MiB per GPU): the call allocates nothing, for callers
+    that cannot (graph capture, serving loops).  Pass `out` (and `lse`) to keep
+    this wrapper from allocating them.  Calls that overlap on one GPU race."""
+    q4 = q.unsqueeze(1) if q.dim() == 3 else q
+    _dev(q4, "q", torch.bfloat16, 4)
+    f8 = k_scale is not None
+    if (k_scale is None) != (v_scale is None):
+        raise ValueError("give both k_scale and v_scale (FP8 caches) or neither (bf16 caches)")
+    _dev(k_cache, "k_cache", torch.uint8 if f8 else torch.bfloat16, 4)
+    _dev(v_cache, "v_cache", torch.uint8 if f8 else torch.bfloat16, 4)
+    _dev(seq_lens, "seq_lens", torch.int32, 1)
+    _dev(sinks, "sinks", torch.float32, 1)
+    if k_cache.stride() != v_cache.stride() or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must share shape and strides")
+    if q4.stride(3) != 1 or k_cache.stride(3) != 1:
+        raise ValueError("q and the caches need unit stride along head_dim")
+    B, q_len, Hq, D = q4.shape
+    Hkv = k_cache.shape[1]
+    if f8:
+        _fp8_scales(k_scale, v_scale, Hkv)
+    max_ctx = k_cache.shape[2] if max_ctx is None else int(max_ctx)
+    if num_splits is None:
+        num_splits = -(-max_ctx // split_size)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    out4 = out.unsqueeze(1) if out.dim() == 3 else out
+    _dev(out4, "out", torch.bfloat16, 4)
+    if tuple(out4.shape) != (B, q_len, Hq, D) or out4.stride(3) != 1:
+        raise ValueError("out must match q's shape with unit stride along head_dim")
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+        if not lse.is_contiguous() or lse.numel() != B * q_len * Hq:
+            raise ValueError("lse must be a contiguous fp32 tensor of B * q_len * Hq rows")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = load_library().sink_attn_decode_merged_noalloc(
+        q4.data_ptr(), q4.stride(0), q4.stride(1), q4.stride(2), q_len, k_cache.data_ptr(),
+        v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1), k_cache.stride(2),
+        None if k_scale is None else k_scale.data_ptr(),
+        None if v_scale is None else v_scale.data_ptr(), seq_lens.data_ptr(), B, max_ctx,
+        sinks.data_ptr(), Hq, Hkv, D, scale, int(split_size), int(num_splits), out4.data_ptr(),
+        out4.stride(0), out4.stride(1), out4.stride(2),
+        lse.data_ptr() if lse is not None else None, _stream(stream))
+    _check("sink_attn_decode_merged_noalloc", rc)
+    return out

@@ -148,7 +148,8 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
                               float* part_o, float* part_m, float* part_d, void* stream,
                               int32_t* counters = nullptr, void* o = nullptr, int64_t o_stride_b = 0,
                               int64_t o_stride_tok = 0, int64_t o_stride_head = 0,
-                              float* lse = nullptr, bool merged = false) {
+                              float* lse = nullptr, bool merged = false,
+                              bool use_scratch = false) {
   const bool fp8 = k_scale != nullptr || v_scale != nullptr;
   const bool fused = counters != nullptr || o != nullptr;
   const bool paged = page_size != 0;
@@ -175,8 +176,8 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
     return fail(SINK_ATTN_EUNSUPPORTED, "split_size %d spans more than 255 pages of %d tokens",
                 split_size, page_size);
   if (batch == 0) return SINK_ATTN_OK;
-  if (!q || !k_cache || !v_cache || !seq_lens || !sinks || !part_o || !part_m || !part_d ||
-      (paged && !block_tables))
+  if (!q || !k_cache || !v_cache || !seq_lens || !sinks ||
+      (!use_scratch && (!part_o || !part_m || !part_d)) || (paged && !block_tables))
     return fail(SINK_ATTN_EINVAL, "a required pointer is null");
   if (paged && !aligned(block_tables, 4))
     return fail(SINK_ATTN_EINVAL, "block_tables must be 4-byte aligned");
@@ -192,7 +193,7 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return fail(SINK_ATTN_EINVAL, "q, k_cache and v_cache must be 16-byte aligned");
   if (!aligned(seq_lens, 4) || !aligned(sinks, 4) || !aligned(part_o, 4) || !aligned(part_m, 4) ||
-      !aligned(part_d, 4))
+      !aligned(part_d, 4))   // (null when the scratch array holds them)
     return fail(SINK_ATTN_EINVAL, "seq_lens, sinks and the partial buffers must be 4-byte aligned");
   if (!stride_ok(q_stride_b) || !stride_ok(q_stride_tok) || !stride_ok(q_stride_head))
     return fail(SINK_ATTN_EINVAL, "query strides must be non-negative multiples of 8 elements");
@@ -214,6 +215,23 @@ static int decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_strid
   const int64_t num_blocks = static_cast<int64_t>(batch) * num_kv_heads * head_slices * num_splits;
   if (ncols > 0x7fffffff || num_blocks > 0x7fffffff)
     return fail(SINK_ATTN_EUNSUPPORTED, "problem too large for one launch");
+  if (use_scratch) {
+    // the chunk states live in the library's device scratch array
+    const int64_t rows = static_cast<int64_t>(batch) * q_len * num_q_heads;
+    const int64_t need = rows * num_splits * (head_dim + 2);
+    if (need > sinkattn::kDecodeScratchFloats)
+      return fail(SINK_ATTN_EINVAL,
+                  "the chunk states need %lld fp32 (batch * q_len * num_q_heads * num_splits * "
+                  "(head_dim + 2)); the scratch holds %lld",
+                  static_cast<long long>(need), static_cast<long long>(sinkattn::kDecodeScratchFloats));
+    float* base = nullptr;
+    const hipError_t e = sinkattn::decode_scratch(&base);
+    if (e != hipSuccess)
+      return fail(SINK_ATTN_ELAUNCH, "device address of the scratch array: %s", hipGetErrorString(e));
+    part_o = base;
+    part_m = base + rows * num_splits * head_dim;
+    part_d = part_m + rows * num_splits;
+  }
 
   sinkattn::DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
@@ -348,6 +366,29 @@ int sink_attn_decode_merged(const void* q, int64_t q_stride_b, int64_t q_stride_
                             0, seq_lens, batch, max_ctx, sinks, num_q_heads, num_kv_heads,
                             head_dim, scale, split_size, num_splits, part_o, part_m, part_d,
                             stream, nullptr, o, o_stride_b, o_stride_tok, o_stride_head, lse, true);
+}
+
+int sink_attn_decode_merged_noalloc(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                                    int64_t q_stride_head, int32_t q_len, const void* k_cache,
+                                    const void* v_cache, int64_t kv_stride_b,
+                                    int64_t kv_stride_head, int64_t kv_stride_tok,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                                    const float* sinks, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, float scale,
+                                    int32_t split_size, int32_t num_splits, void* o,
+                                    int64_t o_stride_b, int64_t o_stride_tok,
+                                    int64_t o_stride_head, float* lse, void* stream) {
+  g_err[0] = '\0';
+  if ((k_scale == nullptr) != (v_scale == nullptr))
+    return fail(SINK_ATTN_EINVAL, "k_scale and v_scale must both be given or both be null");
+  if (batch > 0 && !o) return fail(SINK_ATTN_EINVAL, "a required pointer is null");
+  return decode_multi_split(q, q_stride_b, q_stride_tok, q_stride_head, q_len, k_cache, v_cache,
+                            kv_stride_b, kv_stride_head, kv_stride_tok, k_scale, v_scale, nullptr, 0,
+                            0, seq_lens, batch, max_ctx, sinks, num_q_heads, num_kv_heads,
+                            head_dim, scale, split_size, num_splits, nullptr, nullptr, nullptr,
+                            stream, nullptr, o, o_stride_b, o_stride_tok, o_stride_head, lse, true,
+                            true);
 }
 
 int sink_attn_decode_paged_split(const void* q, int64_t q_stride_b, int64_t q_stride_tok,

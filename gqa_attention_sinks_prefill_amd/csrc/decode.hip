@@ -43,6 +43,8 @@
 // merge_rows_kernel (up to 16 chunks) and merge_kernel: log-sum-exp weighted
 // sum of the chunk states, rounded to bf16 -- D / 4 lanes per (b, h) row, or
 // one wave per row with lane = d.
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -827,6 +829,32 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 }
 
 }  // namespace
+
+// Scratch of the no-allocation decode entry point: the chunk states (o, m, d)
+// of one call, carved from this array.  Each GPU the library runs on holds its
+// own copy (kDecodeScratchFloats fp32, 128 MiB) until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory: its
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[kDecodeScratchFloats];
+
+hipError_t decode_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
 
 int decode_column_blocks(int ncols, int head_dim) {
   const int need = (ncols + 15) / 16;

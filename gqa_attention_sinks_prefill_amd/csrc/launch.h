@@ -124,6 +124,10 @@ int decode_split_size(int64_t column_units, int max_ctx, int head_dim, int cus);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,
                                hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);
+// fp32 elements of the device scratch array behind the no-allocation decode,
+// and its address on the current device (looked up once per device).
+constexpr int64_t kDecodeScratchFloats = int64_t(1) << 25;
+hipError_t decode_scratch(float** out);
 int kv_append_tokens_per_block(int head_dim);
 hipError_t launch_kv_append(const KvAppendArgs& a, int head_dim, int64_t num_blocks,
                             hipStream_t stream);

@@ -317,6 +317,37 @@ int sink_attn_decode_merged(const void* q, int64_t q_stride_b, int64_t q_stride_
                             float* lse, void* stream);
 
 /*
+ * sink_attn_decode_merged without the caller's partial buffers, for callers
+ * that cannot allocate device memory around the call: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The chunk
+ * states live in a device array the library holds on each GPU it runs on
+ * (2^25 fp32 = 128 MiB, kept until the process ends); the call itself
+ * allocates and frees nothing.
+ *   Arguments, outputs and results as sink_attn_decode_merged (bitwise the
+ *   same o and lse), minus part_o / part_m / part_d.
+ *   Limit: batch * q_len * num_q_heads * num_splits * (head_dim + 2) <= 2^25,
+ *   else SINK_ATTN_EINVAL (nothing enqueued).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (concurrent streams, threads) race and give undefined results; calls
+ *   ordered on one stream are safe.  Nothing in the array needs to start at
+ *   zero (every state the merge reads is written by the same call).  The
+ *   array is found on the device current at the call (stream must belong to
+ *   it); the first call on a device looks up its address
+ *   (SINK_ATTN_ELAUNCH if that fails).
+ */
+int sink_attn_decode_merged_noalloc(const void* q, int64_t q_stride_b, int64_t q_stride_tok,
+                                    int64_t q_stride_head, int32_t q_len, const void* k_cache,
+                                    const void* v_cache, int64_t kv_stride_b,
+                                    int64_t kv_stride_head, int64_t kv_stride_tok,
+                                    const float* k_scale, const float* v_scale,
+                                    const int32_t* seq_lens, int32_t batch, int32_t max_ctx,
+                                    const float* sinks, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, float scale,
+                                    int32_t split_size, int32_t num_splits, void* o,
+                                    int64_t o_stride_b, int64_t o_stride_tok,
+                                    int64_t o_stride_head, float* lse, void* stream);
+
+/*
  * FP8 KV cache.  The pages speak of FP8 only for weights; decode, though, is
  * bound by the bytes of the cache it streams ("Hosting Qwen on Blackwell",
  * section "Decoders"), and one byte per element halves them.  Format: OCP FP8

@@ -516,3 +516,41 @@ def test_decode_split_size_follows_the_launch_shape():
     assert sa.sink_attn_decode_split_size(32, 32768, 64, 8, 64) == 2048
     assert sa.sink_attn_decode_split_size(128, 32768, 64, 8, 64) == 2048
 
+
+def _noalloc(**kw):
+    a = dict(q=16, q_sb=4 * 4096, q_st=4096, q_sh=64, q_len=4, k=16, v=16,
+             kv_sb=8 * 1024 * 64, kv_sh=1024 * 64, kv_st=64, ks=None, vs=None, lens=4, batch=4,
+             max_ctx=1024, sinks=4, hq=64, hkv=8, d=64, scale=0.125, split=256, nsplit=4,
+             o=32, o_sb=4 * 4096, o_st=4096, o_sh=64, lse=None)
+    a.update(kw)
+    lib = sa.load_library()
+    rc = lib.sink_attn_decode_merged_noalloc(
+        a["q"], a["q_sb"], a["q_st"], a["q_sh"], a["q_len"], a["k"], a["v"], a["kv_sb"],
+        a["kv_sh"], a["kv_st"], a["ks"], a["vs"], a["lens"], a["batch"], a["max_ctx"],
+        a["sinks"], a["hq"], a["hkv"], a["d"], a["scale"], a["split"], a["nsplit"], a["o"],
+        a["o_sb"], a["o_st"], a["o_sh"], a["lse"], None)
+    return rc, lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(ks=4), -1, "both"),
+    (dict(o=None), -1, "null"),
+    (dict(q=None), -1, "null"),
+    (dict(o=40), -1, "aligned"),
+    (dict(o_st=100), -1, "multiples of 8"),
+    (dict(q_len=0), -1, "q_len"),
+    (dict(nsplit=2), -1, "cover"),
+    (dict(d=32), -2, "head_dim"),
+    # 4 * 4 * 64 * 2048 * 66 fp32 of chunk states: past the 2^25 of the scratch
+    (dict(nsplit=2048), -1, "scratch"),
+    (dict(batch=1 << 16, nsplit=4), -1, "scratch"),
+])
+def test_decode_merged_noalloc_rejects_bad_arguments(kw, code, needle):
+    # every case fails on the host, before the scratch address is looked up
+    rc, msg = _noalloc(**kw)
+    assert rc == code and needle in msg, (rc, msg)
+
+
+def test_decode_merged_noalloc_empty_batch_is_a_noop():
+    rc, msg = _noalloc(batch=0, q=None, k=None, v=None, lens=None, sinks=None, o=None)
+    assert rc == 0, msg
