@@ -27,9 +27,11 @@ After the timed steps (not part of them): `hbm_read_reference` times a plain
 streaming-read kernel (libhbmprobe.so) and `decode.frac_of_measured_read`
 relates the decode to it; `extra` holds the other workloads' lines -- the
 head_dim 128 varlen prefill, chunked prefill, multi-token decode, decode over
-FP8 caches and over 16-token pages, KV-cache append, the ragged
-long-context decode at B = 1, 8, 32, 128 (with the library's split size;
-B < 32 is latency bound and flagged so) and the one-launch decode
+FP8 caches and over 16-token pages (these three with the library's chunk
+size, sink_attn_decode_split_size, and 1024-token chunks beside it), the
+split-KV decode shape with the library's chunk size, KV-cache append, the
+ragged long-context decode at B = 1, 8, 32, 128 (library's chunk size; B < 32
+is latency bound and flagged so) and the one-launch decode
 (sink_attn_decode_fused) beside split + merge; the ragged, one-launch and
 append lines take device time from HIP-graph replay and cycle through copies
 of their inputs so that each round of calls touches at least 4 GiB.
@@ -290,129 +292,163 @@ def kv_append_measurement(dev, stream, reps: int):
             "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def _decode_line(name, metric, kv, chosen, times, copies, extra=None):
+    """One decode line: the value at the library's chunk size, 1024 beside it."""
+    ms = times[chosen]
+    gbs = kv / (ms * 1e-3) / 1e9
+    line = {"workload": name, "value": round(gbs, 1), "unit": "GB/s", "metric": metric,
+            "split_size": chosen, "mean_ms": round(ms, 4),
+            "split1024_ms_same_run": round(times[1024], 4),
+            "split1024_gbs": round(kv / (times[1024] * 1e-3) / 1e9, 1),
+            "algorithmic_bytes_per_step": kv, "cache_copies_rotated": copies,
+            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    line.update(extra or {})
+    return line
+
+
+def _partials(B, q_len, Hq, ns, D, dev):
+    return (torch.empty(B, q_len, Hq, ns, D, device=dev), torch.empty(B, q_len, Hq, ns, device=dev),
+            torch.empty(B, q_len, Hq, ns, device=dev))
+
+
 def multi_decode_measurement(dev, stream, reps: int):
     """KV GB/s of multi-token decode (speculative / MTP verification): 64 requests x
-    8192 cached tokens, the last 4 of them new, split 1024 + merge, event-timed."""
+    8192 cached tokens, the last 4 of them new, split decode + merge with the
+    library's chunk size for these (equal) lengths, 1024-token chunks beside it;
+    device time from graph replay over rotated cache copies."""
     cfg = wl.MTP_DECODE
     inp = wl.decode_inputs(cfg)
-    q, kc, vc = inp["q"].to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev)
-    lens, sinks = inp["seq_lens"].to(dev), inp["sinks"].to(dev)
+    q, lens, sinks = inp["q"].to(dev), inp["seq_lens"].to(dev), inp["sinks"].to(dev)
     B, q_len, Hq, D = q.shape
-    ns = cfg.num_splits
-    po = torch.empty(B, q_len, Hq, ns, D, device=dev)
-    pm = torch.empty(B, q_len, Hq, ns, device=dev)
-    pd = torch.empty(B, q_len, Hq, ns, device=dev)
-    out = torch.empty(B, q_len, Hq, D, dtype=torch.bfloat16, device=dev)
-    run = lambda: sa.sink_attn_decode_multi(q, kc, vc, lens, sinks, cfg.split_size, ns,
-                                            scale=cfg.scale, out=out, partials=(po, pm, pd),
-                                            stream=stream)
-    for _ in range(10):
-        run()
-    torch.cuda.synchronize()
-    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-         for _ in range(reps)]
-    for a, b in e:
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
     kv = wl.decode_kv_bytes(inp["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
-    gbs = kv / (ms * 1e-3) / 1e9
-    return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
-            "metric": "multi-token decode KV GB/s (split + merge)", "mean_ms": round(ms, 4),
-            "algorithmic_bytes_per_step": kv,
-            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    n = rotation(kv)
+    caches = [(inp["k_cache"].to(dev), inp["v_cache"].to(dev))]
+    caches += [(caches[0][0].clone(), caches[0][1].clone()) for _ in range(n - 1)]
+    out = torch.empty(B, q_len, Hq, D, dtype=torch.bfloat16, device=dev)
+    chosen = sa.sink_attn_decode_split_size(B, cfg.max_ctx, Hq, cfg.num_kv_heads, D, q_len,
+                                            seq_lens=inp["seq_lens"])
+    times = {}
+    for split in sorted({1024, chosen}):
+        ns = -(-cfg.max_ctx // split)
+        part = _partials(B, q_len, Hq, ns, D, dev)
+
+        def run(s, i, split=split, ns=ns, part=part):
+            kc, vc = caches[i % n]
+            sa.sink_attn_decode_multi(q, kc, vc, lens, sinks, split, ns, scale=cfg.scale,
+                                      out=out, partials=part, stream=s)
+        times[split] = graph_ms(run, stream, reps=max(3, reps // 2))
+        del part
+    del caches
+    torch.cuda.empty_cache()
+    return _decode_line("mtp_decode_b64_q4_ctx8192_h64kv8_d64",
+                        "multi-token decode KV GB/s (split + merge, graph replay)", kv, chosen,
+                        times, n)
 
 
 def fp8_decode_measurement(dev, stream, reps: int):
     """Decode over FP8 (E4M3) caches: 64 requests x 8192 tokens, 64 / 8 heads,
-    d 64, split 1024 + merge, event-timed.  GB/s of the one-byte codes read
+    d 64, split decode + merge with the library's chunk size (1024 beside it),
+    graph replay over rotated cache copies.  GB/s of the one-byte codes read
     (half the bytes of the bf16 line for the same tokens)."""
     cfg = wl.FP8_DECODE
     inp = wl.fp8_decode_inputs(cfg)
-    q, kc, vc = inp["q"].to(dev), inp["k_cache"].to(dev), inp["v_cache"].to(dev)
+    q, lens, sinks = inp["q"].to(dev), inp["seq_lens"].to(dev), inp["sinks"].to(dev)
     ks, vs = inp["k_scale"].to(dev), inp["v_scale"].to(dev)
-    lens, sinks = inp["seq_lens"].to(dev), inp["sinks"].to(dev)
     B, Hq, D = q.shape
-    ns = cfg.num_splits
-    po = torch.empty(B, 1, Hq, ns, D, device=dev)
-    pm = torch.empty(B, 1, Hq, ns, device=dev)
-    pd = torch.empty(B, 1, Hq, ns, device=dev)
-    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
-    run = lambda: sa.sink_attn_decode_fp8(q, kc, vc, ks, vs, lens, sinks, cfg.split_size, ns,
-                                          scale=cfg.scale, out=out, partials=(po, pm, pd),
-                                          stream=stream)
-    for _ in range(10):
-        run()
-    torch.cuda.synchronize()
-    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-         for _ in range(reps)]
-    for a, b in e:
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
     kv = wl.decode_kv_bytes_fp8(inp["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
-    gbs = kv / (ms * 1e-3) / 1e9
-    return {"workload": cfg.name, "value": round(gbs, 1), "unit": "GB/s",
-            "metric": "decode FP8 KV GB/s (split + merge)", "mean_ms": round(ms, 4),
-            "algorithmic_bytes_per_step": kv,
-            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    n = rotation(kv)
+    caches = [(inp["k_cache"].to(dev), inp["v_cache"].to(dev))]
+    caches += [(caches[0][0].clone(), caches[0][1].clone()) for _ in range(n - 1)]
+    out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    chosen = sa.sink_attn_decode_split_size(B, cfg.max_ctx, Hq, cfg.num_kv_heads, D,
+                                            seq_lens=inp["seq_lens"])
+    times = {}
+    for split in sorted({1024, chosen}):
+        ns = -(-cfg.max_ctx // split)
+        part = _partials(B, 1, Hq, ns, D, dev)
+
+        def run(s, i, split=split, ns=ns, part=part):
+            kc, vc = caches[i % n]
+            sa.sink_attn_decode_fp8(q, kc, vc, ks, vs, lens, sinks, split, ns, scale=cfg.scale,
+                                    out=out, partials=part, stream=s)
+        times[split] = graph_ms(run, stream, reps=max(3, reps // 2))
+        del part
+    del caches
+    torch.cuda.empty_cache()
+    return _decode_line("fp8_decode_b64_ctx8192_h64kv8_d64",
+                        "decode FP8 KV GB/s (split + merge, graph replay)", kv, chosen, times, n)
 
 
 def paged_decode_measurement(dev, stream, reps: int, page_size: int = 16):
     """Decode over a paged bf16 cache: the split-decode shape (64 x 8192, 64 / 8
-    heads, d 64, split 1024 + merge) in 16-token pages under a random block
-    table (seeded), event-timed; GB/s of K/V bytes read."""
+    heads, d 64) in 16-token pages under a random block table (seeded), split
+    decode + merge with the library's chunk size (capped at the 254 pages a
+    chunk may span; 1024 beside it), graph replay over rotated page pools;
+    GB/s of K/V bytes read."""
     cfg = wl.SPLIT_DECODE
     inp = wl.decode_inputs(cfg)
     B, Hkv, L, D = inp["k_cache"].shape
     per = L // page_size
     g = torch.Generator().manual_seed(9)
     perm = torch.randperm(B * per, generator=g).view(B, per).to(torch.int32)
+    kv = wl.decode_kv_bytes(inp["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
+    n = rotation(kv)
     # page p of request b holds its tokens p*P .. p*P+P-1 (one scatter on the GPU)
     kc, vc = inp["k_cache"].to(dev), inp["v_cache"].to(dev)
     kp = torch.empty(B * per, Hkv, page_size, D, dtype=torch.bfloat16, device=dev)
     vp = torch.empty_like(kp)
-    src_k = kc.view(B, Hkv, per, page_size, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page_size, D)
-    src_v = vc.view(B, Hkv, per, page_size, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page_size, D)
     idx = perm.view(-1).to(dev).long()
-    kp[idx] = src_k
-    vp[idx] = src_v
-    del kc, vc, src_k, src_v
+    kp[idx] = kc.view(B, Hkv, per, page_size, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page_size, D)
+    vp[idx] = vc.view(B, Hkv, per, page_size, D).permute(0, 2, 1, 3, 4).reshape(B * per, Hkv, page_size, D)
+    del kc, vc
+    pools = [(kp, vp)] + [(kp.clone(), vp.clone()) for _ in range(n - 1)]
     bt = perm.to(dev)
     q, lens, sinks = inp["q"].to(dev), inp["seq_lens"].to(dev), inp["sinks"].to(dev)
     Hq = q.shape[1]
-    ns = cfg.num_splits
-    po = torch.empty(B, 1, Hq, ns, D, device=dev)
-    pm = torch.empty(B, 1, Hq, ns, device=dev)
-    pd = torch.empty(B, 1, Hq, ns, device=dev)
     out = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
-    run = lambda: sa.sink_attn_decode_paged(q, kp, vp, bt, lens, sinks, cfg.split_size, ns,
-                                            scale=cfg.scale, out=out, partials=(po, pm, pd),
-                                            stream=stream)
-    for _ in range(10):
-        run()
-    torch.cuda.synchronize()
-    e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-         for _ in range(reps)]
-    for a, b in e:
-        a.record(stream)
-        run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
-    kv = wl.decode_kv_bytes(inp["seq_lens"].tolist(), cfg.num_kv_heads, cfg.head_dim)
-    gbs = kv / (ms * 1e-3) / 1e9
-    del kp, vp
+    cap = 1 << ((254 * page_size).bit_length() - 1)      # largest power of two <= 254 pages
+    chosen = min(cap, sa.sink_attn_decode_split_size(B, L, Hq, Hkv, D, seq_lens=inp["seq_lens"]))
+    times = {}
+    for split in sorted({1024, chosen}):
+        ns = -(-L // split)
+        part = _partials(B, 1, Hq, ns, D, dev)
+
+        def run(s, i, split=split, ns=ns, part=part):
+            k_, v_ = pools[i % n]
+            sa.sink_attn_decode_paged(q, k_, v_, bt, lens, sinks, split, ns, scale=cfg.scale,
+                                      out=out, partials=part, stream=s)
+        times[split] = graph_ms(run, stream, reps=max(3, reps // 2))
+        del part
+    del pools, kp, vp
     torch.cuda.empty_cache()
-    return {"workload": f"paged_decode_b64_ctx8192_page{page_size}_h64kv8_d64_split1024",
-            "value": round(gbs, 1), "unit": "GB/s",
-            "metric": "paged decode KV GB/s (split + merge)", "mean_ms": round(ms, 4),
-            "algorithmic_bytes_per_step": kv,
-            "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+    return _decode_line(f"paged_decode_b64_ctx8192_page{page_size}_h64kv8_d64",
+                        "paged decode KV GB/s (split + merge, graph replay)", kv, chosen, times, n,
+                        {"split_cap_pages": 254})
+
+
+def library_split_decode_measurement(dev, stream, reps: int):
+    """The split-KV decode shape (64 requests x 8192 tokens, 64 / 8 heads, d 64)
+    through the length-aware split + merge with the library's chunk size for
+    these equal lengths (1024-token chunks beside it), graph replay over rotated
+    cache copies."""
+    cfg = wl.SPLIT_DECODE
+    chosen = sa.sink_attn_decode_split_size(cfg.batch, cfg.max_ctx, cfg.num_q_heads,
+                                            cfg.num_kv_heads, cfg.head_dim,
+                                            seq_lens=[cfg.ctx] * cfg.batch)
+    x = _decode_buffers(cfg, dev, chosen)
+    times = {chosen: graph_ms(_merged(cfg, x), stream, reps=max(3, reps // 2))}
+    if chosen != 1024:
+        B, Hq, D = x["q"].shape
+        x1 = dict(x, split=1024, ns=cfg.num_splits,
+                  part=tuple(t.view(B, Hq, *t.shape[3:]) for t in _partials(B, 1, Hq, cfg.num_splits, D, dev)))
+        times[1024] = graph_ms(_merged(cfg, x1), stream, reps=max(3, reps // 2))
+        del x1
+    kv, n = x["kv"], len(x["caches"])
+    del x
+    torch.cuda.empty_cache()
+    return _decode_line(cfg.name.replace("_split1024", "") + "_library_split",
+                        "decode KV GB/s (length-aware split + merge, graph replay)", kv, chosen,
+                        times, n)
 
 
 def hbm_read_reference(dev, stream, reps: int = 10):
@@ -548,9 +584,16 @@ def ragged_decode_measurement(dev, stream, batch: int, reps: int, keep: dict | N
     one more call (with lse) leaves the CPU inputs and the outputs there for
     the oracle leg."""
     cfg = wl.ragged_decode(batch)
+    x = _decode_buffers(cfg, dev)
     split = sa.sink_attn_decode_split_size(batch, cfg.max_ctx, cfg.num_q_heads,
-                                           cfg.num_kv_heads, cfg.head_dim)
-    x = _decode_buffers(cfg, dev, split)
+                                           cfg.num_kv_heads, cfg.head_dim,
+                                           seq_lens=x["cpu"]["seq_lens"])
+    if split != cfg.split_size:
+        B, Hq, D = x["q"].shape
+        ns = -(-cfg.max_ctx // split)
+        x.update(split=split, ns=ns, part=(torch.empty(B, Hq, ns, D, device=dev),
+                                           torch.empty(B, Hq, ns, device=dev),
+                                           torch.empty(B, Hq, ns, device=dev)))
     reps = max(3, reps // 2)
     two = graph_ms(_split_merge(cfg, x), stream, reps=reps)
     ms = graph_ms(_merged(cfg, x), stream, reps=reps)
@@ -801,6 +844,7 @@ def main():
                 lambda: multi_decode_measurement(dev, stream, r2),
                 lambda: fp8_decode_measurement(dev, stream, r2),
                 lambda: paged_decode_measurement(dev, stream, r2),
+                lambda: library_split_decode_measurement(dev, stream, r2),
                 lambda: kv_append_measurement(dev, stream, r2)]
         jobs += [lambda b=b: ragged_decode_measurement(dev, stream, b, r4, keep=keep_ragged[b])
                  for b in wl.RAGGED_BATCHES]

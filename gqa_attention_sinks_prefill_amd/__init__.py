@@ -118,7 +118,7 @@ def load_library():
     # ... and without the partial buffers either
     lib.sink_attn_decode_merged_noalloc.argtypes = fused[:22] + fused[26:]
     lib.sink_attn_decode_merged_noalloc.restype = ctypes.c_int
-    lib.sink_attn_decode_split_size.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.sink_attn_decode_split_size.argtypes = [I32, I32, I32, I32, I32, I32, P]
     lib.sink_attn_decode_split_size.restype = ctypes.c_int32
     lib.sink_attn_last_error.argtypes = []
     lib.sink_attn_last_error.restype = ctypes.c_char_p
@@ -644,12 +644,21 @@ def sink_attn_kv_append_paged(k_new, v_new, cu_seqlens_new, cache_pos, k_pages, 
     return k_pages, v_pages
 
 
-def sink_attn_decode_split_size(batch, max_ctx, num_q_heads, num_kv_heads, head_dim, q_len=1):
+def sink_attn_decode_split_size(batch, max_ctx, num_q_heads, num_kv_heads, head_dim, q_len=1,
+                                seq_lens=None):
     """Tokens per chunk for split-KV decode of this launch shape (the library's
-    choice: 1024, or 2048 when that still gives every SIMD four work units)."""
+    choice).  seq_lens: the request lengths on the host (list, array or CPU
+    tensor) when the caller has them -- equal lengths get long chunks -- else
+    None (treated as ragged)."""
+    ptr, keep = None, None
+    if seq_lens is not None:
+        keep = torch.as_tensor(seq_lens, dtype=torch.int32).cpu().contiguous()
+        if keep.numel() != int(batch):
+            raise ValueError("seq_lens needs one length per request")
+        ptr = keep.data_ptr()
     rc = load_library().sink_attn_decode_split_size(int(batch), int(max_ctx), int(q_len),
                                                     int(num_q_heads), int(num_kv_heads),
-                                                    int(head_dim))
+                                                    int(head_dim), ptr)
     if rc <= 0:
         _check("sink_attn_decode_split_size", rc if rc != 0 else -1)
     return int(rc)

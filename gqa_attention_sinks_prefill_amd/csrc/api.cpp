@@ -432,11 +432,29 @@ int sink_attn_decode_split(const void* q, int64_t q_stride_b, int64_t q_stride_h
 }
 
 int32_t sink_attn_decode_split_size(int32_t batch, int32_t max_ctx, int32_t q_len,
-                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    const int32_t* seq_lens_host) {
   g_err[0] = '\0';
   if (batch < 0 || max_ctx < 0) return fail(SINK_ATTN_EINVAL, "batch and max_ctx must be >= 0");
   if (q_len < 1) return fail(SINK_ATTN_EINVAL, "q_len must be >= 1 (got %d)", q_len);
   if (int rc = check_heads(num_q_heads, num_kv_heads, head_dim)) return rc;
+  // with the lengths: their longest, and whether they are (nearly) equal
+  int max_len = max_ctx;
+  bool uniform = false;
+  if (seq_lens_host != nullptr && batch > 0) {
+    int64_t total = 0;
+    int longest = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t len = seq_lens_host[b];
+      if (len < 0 || len > max_ctx)
+        return fail(SINK_ATTN_EINVAL, "seq_lens_host[%d] = %d is outside [0, max_ctx = %d]", b, len,
+                    max_ctx);
+      total += len;
+      longest = len > longest ? len : longest;
+    }
+    max_len = longest;
+    uniform = longest > 0 && 10 * total >= 9 * static_cast<int64_t>(batch) * longest;
+  }
   int device = 0, cus = 0;
   if (hipGetDevice(&device) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
@@ -446,8 +464,8 @@ int32_t sink_attn_decode_split_size(int32_t batch, int32_t max_ctx, int32_t q_le
   const int cols_per_block = 16 * sinkattn::decode_column_blocks(
       static_cast<int>(ncols > 0x7fffffff ? 0x7fffffff : ncols), head_dim);
   const int64_t slices = (ncols + cols_per_block - 1) / cols_per_block;
-  return sinkattn::decode_split_size(static_cast<int64_t>(batch) * num_kv_heads * slices, max_ctx,
-                                     head_dim, cus);
+  return sinkattn::decode_split_size(static_cast<int64_t>(batch) * num_kv_heads * slices, max_len,
+                                     uniform, head_dim, cus);
 }
 
 int sink_attn_merge_states(const float* part_o, const float* part_m, const float* part_d,

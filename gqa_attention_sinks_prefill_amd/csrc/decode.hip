@@ -878,19 +878,28 @@ int decode_waves_per_unit(int64_t num_units, int head_dim, int column_blocks) {
   return num_units >= simds ? 1 : (2 * num_units >= simds ? 2 : 4);
 }
 
-int decode_split_size(int64_t column_units, int max_ctx, int head_dim, int cus) {
-  // 1024-token chunks, or 2048 when even those give every SIMD four units at
-  // the longest context.  Measured (ragged contexts U[1024, 32768], d 64,
-  // length-aware split + merge, graph replay): B = 128 / 32 ran 748 / 188 us
-  // with 2048 against 788 / 191 with 1024 (fewer chunk states, longer runs of
-  // one head per wave); B = 8 / 1 ran 69 / 25 us with 2048 against 59 / 17
-  // with 1024, and smaller chunks were slower at every batch size (B = 1:
-  // 19 us at 512, 24 at 256), the per-unit work (query load, state write,
-  // merge input) outweighing the extra parallelism.
+int decode_split_size(int64_t column_units, int max_len, bool uniform, int head_dim, int cus) {
+  // Measured (d 64, split + length-aware merge, graph replay, inputs rotated
+  // past the Infinity Cache):
+  //  * equal contexts want long chunks -- fewer chunk states to write and
+  //    merge, longer runs of one head per wave: 64 x 8192 tokens 171 / 163 /
+  //    160 / 158 us with 1024 / 2048 / 4096 / 8192-token chunks, 4 new tokens
+  //    per request 203 / 181 / 168 / 169 us, FP8 codes 97 / 93 / 96 / 85 us,
+  //    16 x 32768 177 / 164 / 161 / 159 us -- as long as the chunks leave a
+  //    unit for every fourth SIMD;
+  //  * ragged contexts U[1024, 32768] want short ones, the longest requests'
+  //    units otherwise finishing alone: B = 1 / 8 ran 17 / 59 us with 1024,
+  //    25 / 69 with 2048 (smaller chunks were slower still), B = 32 / 128 191
+  //    / 786 us with 1024, 187 / 745 with 2048, 212 / 801 with 4096.
   (void)head_dim;
   const int64_t simds = (int64_t)cus * 4;
-  const int64_t units_2048 = column_units * ((max_ctx + 2047) / 2048);
-  return units_2048 >= 4 * simds ? 2048 : 1024;
+  auto units = [&](int split) { return column_units * ((max_len + split - 1) / split); };
+  if (uniform) {
+    int split = 8192;
+    while (split > 1024 && (split / 2 >= max_len || units(split) < simds / 4)) split /= 2;
+    return split;
+  }
+  return units(2048) >= 4 * simds ? 2048 : 1024;
 }
 
 template <int D, int CB, bool F8, bool PG>

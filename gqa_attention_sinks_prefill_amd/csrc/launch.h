@@ -118,9 +118,9 @@ int decode_column_blocks(int ncols, int head_dim);
 // Waves (1, 2 or 4) that share one decode work unit.
 int decode_waves_per_unit(int64_t num_units, int head_dim, int column_blocks);
 // Tokens per chunk for split decode of `column_units` (request, KV head,
-// column slice) triples over contexts of at most max_ctx tokens on `cus`
-// compute units.
-int decode_split_size(int64_t column_units, int max_ctx, int head_dim, int cus);
+// column slice) triples over contexts of at most max_len tokens on `cus`
+// compute units; `uniform`: the contexts are (nearly) all max_len long.
+int decode_split_size(int64_t column_units, int max_len, bool uniform, int head_dim, int cus);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int64_t num_blocks,
                                hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, hipStream_t stream);

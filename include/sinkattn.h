@@ -192,21 +192,30 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
 
 /*
  * A chunk size for the split-KV decode calls above and below, chosen from the
- * launch shape alone (the request lengths are device values): "GPT-OSS on day
- * 0", section "Kernels for GPT-OSS / Sink-Attention", parallelises decode over
- * the KV length as well as over heads.  Returns 1024 tokens, or 2048 when
- * chunks of 2048 at the longest context (max_ctx) still give every SIMD of the
- * current device four (request, KV head, column slice, chunk) work units:
- * longer chunks then write fewer chunk states for the merge, while smaller
- * batches keep the parallelism of 1024-token chunks.  Always a positive
- * multiple of 64.  Size the partials with num_splits = ceil(max_ctx / split).
+ * launch shape ("GPT-OSS on day 0", section "Kernels for GPT-OSS /
+ * Sink-Attention": decode is parallelised over the KV length as well as over
+ * heads; the best cut depends on the shape).  The request lengths of a
+ * decode are device values; a caller that also holds them on the host passes
+ * them in seq_lens_host, else NULL.
+ *  - Lengths given and (nearly) equal (their mean >= 0.9 x their longest):
+ *    the longest of 8192, 4096, 2048, 1024 tokens that is needed to cover the
+ *    longest request and still gives every fourth SIMD of the current device
+ *    a (request, KV head, column slice, chunk) unit -- long chunks write fewer
+ *    chunk states for the merge, and equal units finish together.
+ *  - Otherwise (ragged or unknown lengths): 1024, or 2048 when chunks of 2048
+ *    at max_ctx still give every SIMD four units -- short chunks keep a
+ *    ragged batch's longest requests from finishing alone.
+ * Always a positive multiple of 64.  Size the partials with num_splits =
+ * ceil(max_ctx / split).
  *   batch, max_ctx >= 0; q_len >= 1; heads and head_dim as for
- *   sink_attn_decode_multi_split.
+ *   sink_attn_decode_multi_split; seq_lens_host: NULL or batch host int32
+ *   lengths, each in [0, max_ctx].
  * Returns the split size, or SINK_ATTN_EINVAL / SINK_ATTN_EUNSUPPORTED (with a
- * message) for invalid arguments.  Enqueues nothing.
+ * message) for invalid arguments.  Enqueues nothing, reads no device memory.
  */
 int32_t sink_attn_decode_split_size(int32_t batch, int32_t max_ctx, int32_t q_len,
-                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    const int32_t* seq_lens_host);
 
 /*
  * Second half of split-KV decode: merge each row's chunk states by their

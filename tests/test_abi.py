@@ -491,13 +491,16 @@ def test_decode_merged_empty_batch_is_a_noop():
     (dict(q_len=0), -1, "q_len"),
     (dict(hq=6, hkv=4), -1, "multiple"),
     (dict(d=96), -2, "head_dim"),
+    (dict(lens=[100] * 7 + [40000]), -1, "outside"),
+    (dict(lens=[100] * 7 + [-1]), -1, "outside"),
 ])
 def test_decode_split_size_rejects_bad_arguments(kw, code, needle):
-    a = dict(batch=8, max_ctx=32768, q_len=1, hq=64, hkv=8, d=64)
+    a = dict(batch=8, max_ctx=32768, q_len=1, hq=64, hkv=8, d=64, lens=None)
     a.update(kw)
     lib = sa.load_library()
+    lens = None if a["lens"] is None else (ctypes.c_int32 * len(a["lens"]))(*a["lens"])
     rc = lib.sink_attn_decode_split_size(a["batch"], a["max_ctx"], a["q_len"], a["hq"], a["hkv"],
-                                         a["d"])
+                                         a["d"], lens)
     assert rc == code and needle in lib.sink_attn_last_error().decode()
 
 
@@ -507,15 +510,29 @@ def test_decode_split_size_follows_the_launch_shape():
     for batch in (0, 1, 2, 8, 64, 1024):
         for max_ctx in (0, 1, 1000, 8192, 32768, 1 << 20):
             for q_len, hq, hkv, d in ((1, 64, 8, 64), (4, 64, 8, 64), (1, 64, 4, 128)):
-                s = sa.sink_attn_decode_split_size(batch, max_ctx, hq, hkv, d, q_len)
-                assert s in (1024, 2048)
-    # few or short requests keep 1024-token chunks; many long ones get 2048
-    assert sa.sink_attn_decode_split_size(64, 8192, 64, 8, 64) == 1024
-    assert sa.sink_attn_decode_split_size(1, 32768, 64, 8, 64) == 1024
-    assert sa.sink_attn_decode_split_size(8, 32768, 64, 8, 64) == 1024
-    assert sa.sink_attn_decode_split_size(32, 32768, 64, 8, 64) == 2048
-    assert sa.sink_attn_decode_split_size(128, 32768, 64, 8, 64) == 2048
-
+                for lens in (None, [max_ctx] * batch, [max_ctx // (b + 1) for b in range(batch)]):
+                    s = sa.sink_attn_decode_split_size(batch, max_ctx, hq, hkv, d, q_len, lens)
+                    assert s in (1024, 2048, 4096, 8192)
+    split = sa.sink_attn_decode_split_size
+    # ragged or unknown lengths: 1024, or 2048 for many long requests
+    assert split(64, 8192, 64, 8, 64) == 1024
+    assert split(1, 32768, 64, 8, 64) == 1024
+    assert split(8, 32768, 64, 8, 64) == 1024
+    assert split(32, 32768, 64, 8, 64) == 2048
+    assert split(128, 32768, 64, 8, 64) == 2048
+    ragged = [1024 + (31744 * b) // 31 for b in range(32)]
+    assert split(32, 32768, 64, 8, 64, seq_lens=ragged) == 2048
+    assert split(8, 32768, 64, 8, 64, seq_lens=ragged[::4]) == 1024
+    # equal lengths: the longest chunk that covers a request and leaves a unit
+    # for every fourth SIMD
+    assert split(64, 8192, 64, 8, 64, seq_lens=[8192] * 64) == 8192
+    assert split(64, 8192, 64, 8, 64, q_len=4, seq_lens=[8192] * 64) == 8192
+    assert split(16, 32768, 64, 8, 64, seq_lens=[32768] * 16) == 8192
+    assert split(256, 2048, 64, 8, 64, seq_lens=[2048] * 256) == 2048
+    assert split(1, 32768, 64, 8, 64, seq_lens=[32768]) == 1024
+    assert split(4, 32768, 64, 8, 64, seq_lens=[32768] * 4) == 4096
+    assert split(64, 8192, 64, 8, 64, seq_lens=[5000] * 64) == 8192
+    assert split(64, 8192, 64, 8, 64, seq_lens=[3000] * 64) == 4096
 
 def _noalloc(**kw):
     a = dict(q=16, q_sb=4 * 4096, q_st=4096, q_sh=64, q_len=4, k=16, v=16,

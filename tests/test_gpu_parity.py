@@ -257,6 +257,22 @@ def test_decode_split_kv_full_config():
     np.testing.assert_allclose(g_d, d_c, rtol=2e-3)
 
 
+def test_decode_split_kv_shape_library_chunk_size():
+    """The split-KV decode shape (64 x 8192) through sink_attn_decode_merged with
+    the chunk size the library picks for these equal lengths (8192: one chunk
+    per request): every row against the oracle, and bitwise equal to split
+    decode + sink_attn_merge_states at the same chunk size."""
+    cfg = wl.SPLIT_DECODE
+    inp = wl.decode_inputs(cfg)
+    split = sa.sink_attn_decode_split_size(cfg.batch, cfg.max_ctx, cfg.num_q_heads,
+                                           cfg.num_kv_heads, cfg.head_dim, seq_lens=inp["seq_lens"])
+    assert split == 8192
+    out_m, lse_m, _ = _merged_gpu(inp, split)
+    _check_decode(inp, out_m[:, 0], lse_m[:, 0], f"split-KV shape, split {split}")
+    out_s, lse_s, _ = _decode_gpu(inp, split)
+    assert _bitwise(out_m[:, 0], out_s) and torch.equal(lse_m[:, 0], lse_s)
+
+
 def test_decode_is_deterministic():
     cfg = wl.DecodeConfig("det", 8, None, (1, 5000), 5000, 64, 8, 64, (-4.0, 4.0),
                           split_size=1024, seed=5)
@@ -296,7 +312,7 @@ def test_decode_ragged_long_context(batch):
         del po, pm, pd
 
 
-@pytest.mark.parametrize("split", [64, 256, 1024, 4096])
+@pytest.mark.parametrize("split", [64, 256, 1024, 4096, 8192])
 def test_decode_split_size_invariance(split):
     cfg = wl.DecodeConfig("splits", 6, None, (1, 3000), 3000, 16, 2, 64, (-4.0, 4.0),
                           split_size=split, seed=9, edge_sinks={1: float("-inf"), 2: 20.0})
@@ -480,23 +496,21 @@ def test_decode_multi_single_token_matches_decode_split():
     assert torch.equal(lse_m[:, 0], lse_d)
 
 
-def test_decode_multi_full_config_sampled_rows():
-    """64 requests x 8192 tokens, 4 new tokens each (the bench's multi-token line)."""
+def test_decode_multi_full_config_all_rows():
+    """64 requests x 8192 tokens, 4 new tokens each (the bench's multi-token
+    line): every (request, new token, head) row against the oracle, with
+    1024-token chunks and with the library's chunk size for these equal lengths."""
     cfg = wl.MTP_DECODE
     inp = wl.decode_inputs(cfg)
-    out, lse = _decode_multi_gpu(inp, cfg.split_size)
-    assert not torch.isnan(out).any().item()
-    g = torch.Generator().manual_seed(5)
     B, q_len, Hq, D = inp["q"].shape
-    rows = sorted({(int(torch.randint(B, (1,), generator=g)), t, int(torch.randint(Hq, (1,), generator=g)))
-                   for t in range(q_len) for _ in range(40)})
     o_ref, lse_ref, _ = oracle.decode_multi(inp["q"], inp["k_cache"], inp["v_cache"],
-                                            inp["seq_lens"], inp["sinks"], rows=rows)
-    idx = torch.tensor(rows)
-    assert_close(out.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]], o_ref,
-                 what="multi decode full config (sampled rows)")
-    assert_lse_close(lse.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]], lse_ref,
-                     what="multi decode full config lse")
+                                            inp["seq_lens"], inp["sinks"])
+    chosen = sa.sink_attn_decode_split_size(B, cfg.max_ctx, Hq, cfg.num_kv_heads, D, q_len,
+                                            seq_lens=inp["seq_lens"])
+    for split in sorted({cfg.split_size, chosen}):
+        out, lse = _decode_multi_gpu(inp, split)
+        assert_close(out.reshape(-1, D), o_ref, what=f"multi decode full config, split {split}")
+        assert_lse_close(lse.reshape(-1), lse_ref, what=f"multi decode full config lse, split {split}")
 
 
 _EDGE_LENS = [0, 1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 447, 448, 511, 512]
@@ -767,20 +781,19 @@ def test_decode_fp8_work_splits_edge_lengths(B, Hkv, D, q_len, split):
         assert torch.all(pd[b, :, :, first_empty:] == 0)
 
 
-def test_decode_fp8_full_config_sampled_rows():
-    """64 requests x 8192 tokens over FP8 caches (the bench's FP8 decode line)."""
+def test_decode_fp8_full_config_all_rows():
+    """64 requests x 8192 tokens over FP8 caches (the bench's FP8 decode line):
+    every row against the oracle, with 1024-token chunks and with the library's
+    chunk size for these equal lengths."""
     cfg = wl.FP8_DECODE
     inp = wl.fp8_decode_inputs(cfg)
-    out, lse, _ = _fp8_gpu(inp, cfg.split_size)
-    assert not torch.isnan(out).any().item()
-    g = torch.Generator().manual_seed(8)
-    rows = sorted({(int(torch.randint(cfg.batch, (1,), generator=g)), 0,
-                    int(torch.randint(cfg.num_q_heads, (1,), generator=g))) for _ in range(96)}
-                  | {(0, 0, 0), (cfg.batch - 1, 0, cfg.num_q_heads - 1)})
-    o_ref, lse_ref, _ = _fp8_ref(inp, rows=rows)
-    idx = torch.tensor(rows)
-    assert_close(out.cpu()[idx[:, 0], 0, idx[:, 2]], o_ref, what="fp8 decode full config")
-    assert_lse_close(lse.cpu()[idx[:, 0], 0, idx[:, 2]], lse_ref, what="fp8 decode full config lse")
+    o_ref, lse_ref, _ = _fp8_ref(inp)
+    chosen = sa.sink_attn_decode_split_size(cfg.batch, cfg.max_ctx, cfg.num_q_heads,
+                                            cfg.num_kv_heads, cfg.head_dim, seq_lens=inp["seq_lens"])
+    for split in sorted({cfg.split_size, chosen}):
+        out, lse, _ = _fp8_gpu(inp, split)
+        assert_close(out.reshape(-1, cfg.head_dim), o_ref, what=f"fp8 decode full config, split {split}")
+        assert_lse_close(lse.reshape(-1), lse_ref, what=f"fp8 decode full config lse, split {split}")
 
 
 @pytest.mark.parametrize("Hkv,D", [(8, 64), (4, 128), (1, 64)])
@@ -949,8 +962,10 @@ def test_decode_paged_work_splits(B, q_len, fp8):
     assert not torch.isnan(po).any() and not torch.isnan(pm).any()
 
 
-def test_decode_paged_full_config_sampled_rows():
-    """64 requests x 8192 tokens in 16-token pages under a random table."""
+def test_decode_paged_full_config_all_rows():
+    """64 requests x 8192 tokens in 16-token pages under a random table: every
+    row against the oracle, with 1024-token chunks and with the 2048-token
+    chunks the bench uses (the library's choice capped at 254 pages a chunk)."""
     cfg = wl.SPLIT_DECODE
     inp = wl.decode_inputs(cfg)
     g = torch.Generator().manual_seed(150)
@@ -959,14 +974,12 @@ def test_decode_paged_full_config_sampled_rows():
     for b in range(bt.shape[0]):
         for p in range(bt.shape[1]):
             vp[int(bt[b, p])] = inp["v_cache"][b, :, p * 16:(p + 1) * 16]
-    out, lse, _ = _paged_gpu(inp, kp, vp, bt, cfg.split_size, False)
-    rows = sorted({(int(torch.randint(cfg.batch, (1,), generator=g)), 0,
-                    int(torch.randint(cfg.num_q_heads, (1,), generator=g))) for _ in range(64)})
     o_ref, lse_ref, _ = oracle.decode_multi(_q4(inp["q"]), inp["k_cache"], inp["v_cache"],
-                                            inp["seq_lens"], inp["sinks"], rows=rows)
-    idx = torch.tensor(rows)
-    assert_close(out.cpu()[idx[:, 0], 0, idx[:, 2]], o_ref, what="paged decode full config")
-    assert_lse_close(lse.cpu()[idx[:, 0], 0, idx[:, 2]], lse_ref, what="paged decode full config lse")
+                                            inp["seq_lens"], inp["sinks"])
+    for split in (1024, 2048):
+        out, lse, _ = _paged_gpu(inp, kp, vp, bt, split, False)
+        assert_close(out.reshape(-1, cfg.head_dim), o_ref, what=f"paged decode full config, split {split}")
+        assert_lse_close(lse.reshape(-1), lse_ref, what=f"paged decode full config lse, split {split}")
 
 
 @pytest.mark.parametrize("fp8,P,D", [(False, 16, 64), (True, 16, 64), (False, 64, 128), (True, 32, 128)])
