@@ -670,12 +670,12 @@ def main():
                     help="host time budget of the oracle per prefill workload (0 disables the "
                          "oracle leg)")
     ap.add_argument("--only", choices=("all", "prefill", "decode", "varlen", "ragged", "mtp",
-                                       "fp8", "read"),
+                                       "fp8", "paged", "read"),
                     default="all",
                     help="launch only one part of the step, or only the head_dim 128 varlen "
                          "prefill / the B = 128 ragged decode / the multi-token decode / the "
-                         "FP8-cache decode / the streaming-read reference (for hardware-counter "
-                         "runs)")
+                         "FP8-cache decode / the paged decode / the streaming-read reference (for "
+                         "hardware-counter runs)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra workloads' lines (and their oracle checks)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -694,12 +694,13 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev, args.steps)
         return
-    if args.only in ("varlen", "ragged", "mtp", "fp8", "read"):
+    if args.only in ("varlen", "ragged", "mtp", "fp8", "paged", "read"):
         stream = torch.cuda.current_stream()
         line = {"varlen": lambda: varlen_prefill_measurement(dev, stream, args.steps),
                 "ragged": lambda: ragged_decode_measurement(dev, stream, 128, args.steps),
                 "mtp": lambda: multi_decode_measurement(dev, stream, args.steps),
                 "fp8": lambda: fp8_decode_measurement(dev, stream, args.steps),
+                "paged": lambda: paged_decode_measurement(dev, stream, args.steps),
                 "read": lambda: hbm_read_reference(dev, stream, max(3, args.steps))}[args.only]()
         line["note"] = f"--only {args.only}: this workload alone"
         print(json.dumps(line), flush=True)
