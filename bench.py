@@ -23,8 +23,11 @@ split + merge duration, which `decode.roofline` compares with the HBM peak
 (the split kernel alone beside it).  `roofline` compares the prefill kernel
 with the bf16 dense MFMA peak.
 
-After the timed steps (not part of them): `hbm_read_reference` times a plain
-streaming-read kernel (libhbmprobe.so) and `decode.frac_of_measured_read`
+After the timed steps (not part of them): `mfma_rate_reference` times a plain
+loop of bf16 MFMAs on every SIMD over the prefill's own K data (and over
+constant operands), and `roofline.frac_of_measured_mfma` is the prefill's rate
+against it; `hbm_read_reference` times a plain streaming-read kernel
+(libbenchprobes.so) and `decode.frac_of_measured_read`
 relates the decode to it; `extra` holds the other workloads' lines -- the
 head_dim 128 varlen prefill, chunked prefill, multi-token decode, decode over
 FP8 caches and over 16-token pages (these three with the library's chunk
@@ -75,9 +78,13 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
+    """Hash of the library's kernel sources (the benchmark's reference kernels,
+    *_probe.hip, are not part of it)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gqa_attention_sinks_prefill_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if name.endswith("_probe.hip"):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -451,15 +458,21 @@ def library_split_decode_measurement(dev, stream, reps: int):
                         times, n)
 
 
-def hbm_read_reference(dev, stream, reps: int = 10):
-    """GB/s of a plain streaming-read kernel (libhbmprobe.so, built beside the
-    library): 4 GiB read once per launch, each workgroup a contiguous slice,
-    non-temporal 16-byte loads."""
+def probes_lib():
+    """The benchmark's reference kernels (libbenchprobes.so, built beside the library)."""
     import ctypes
-    path = os.path.join(ROOT, "gqa_attention_sinks_prefill_amd", "libhbmprobe.so")
+    path = os.path.join(ROOT, "gqa_attention_sinks_prefill_amd", "libbenchprobes.so")
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: run `python -m gqa_attention_sinks_prefill_amd.build_native`")
-    lib = ctypes.CDLL(path)
+    return ctypes.CDLL(path)
+
+
+def hbm_read_reference(dev, stream, reps: int = 10):
+    """GB/s of a plain streaming-read kernel (libbenchprobes.so): 4 GiB read
+    once per launch, each workgroup a contiguous slice, non-temporal 16-byte
+    loads."""
+    import ctypes
+    lib = probes_lib()
     lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
                                    ctypes.c_void_p, ctypes.c_void_p]
     nbytes, blocks = 4 << 30, 8192
@@ -482,6 +495,47 @@ def hbm_read_reference(dev, stream, reps: int = 10):
     del buf
     return {"kernel": "hbm_read_probe (contiguous slices, non-temporal 16-byte loads, 8192 x 256 threads)",
             "bytes": nbytes, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s"}
+
+
+def mfma_rate_reference(dev, stream, operands: torch.Tensor, reps: int = 5, iters: int = 40000):
+    """TFLOP/s of a plain loop of independent bf16 32x32x16 MFMAs on every SIMD
+    (libbenchprobes.so; 2 waves per SIMD), with operands read from `operands`
+    (a bf16 tensor of the workload: they change from one MFMA to the next, as
+    the prefill's do) and with all operands 1.0.  The chip holds a lower clock
+    while its matrix units switch random data, so the first rate is the
+    ceiling that power leaves for bf16 contractions over such inputs."""
+    import ctypes
+    lib = probes_lib()
+    lib.mfma_rate_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 2 * cus
+    out = torch.zeros(blocks, dtype=torch.int32, device=dev)
+    sp = stream.cuda_stream
+    flop = blocks * 4 * iters * 16 * 2 * 32 * 32 * 16
+    res = {"kernel": f"mfma_rate_probe (v_mfma_f32_32x32x16_bf16 loop, {blocks} x 256 threads, "
+                     f"{iters} x 16 MFMAs per wave)", "unit": "TFLOP/s"}
+    for name, ptr, nbytes in (("workload_operands", operands.data_ptr(),
+                               operands.numel() * operands.element_size()),
+                              ("constant_operands", None, 0)):
+        run = lambda: lib.mfma_rate_probe(ptr, nbytes, blocks, iters, out.data_ptr(), sp)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:       # settle the clock under this load
+            if run() != 0:
+                raise RuntimeError("mfma_rate_probe failed")
+            torch.cuda.synchronize()
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(reps)]
+        for a, b in e:
+            a.record(stream)
+            run()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in e]))
+        res[name] = round(flop / (ms * 1e-3) / 1e12, 1)
+    res["value"] = res["workload_operands"]
+    res["frac_of_peak"] = round(res["workload_operands"] / PEAK_BF16_TFLOPS, 4)
+    return res
 
 
 ROTATE_BYTES = 4 << 30
@@ -670,12 +724,12 @@ def main():
                     help="host time budget of the oracle per prefill workload (0 disables the "
                          "oracle leg)")
     ap.add_argument("--only", choices=("all", "prefill", "decode", "varlen", "ragged", "mtp",
-                                       "fp8", "paged", "read"),
+                                       "fp8", "paged", "read", "mfma"),
                     default="all",
                     help="launch only one part of the step, or only the head_dim 128 varlen "
                          "prefill / the B = 128 ragged decode / the multi-token decode / the "
-                         "FP8-cache decode / the paged decode / the streaming-read reference (for "
-                         "hardware-counter runs)")
+                         "FP8-cache decode / the paged decode / the streaming-read or MFMA-rate "
+                         "reference (for hardware-counter runs)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra workloads' lines (and their oracle checks)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -694,14 +748,17 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev, args.steps)
         return
-    if args.only in ("varlen", "ragged", "mtp", "fp8", "paged", "read"):
+    if args.only in ("varlen", "ragged", "mtp", "fp8", "paged", "read", "mfma"):
         stream = torch.cuda.current_stream()
         line = {"varlen": lambda: varlen_prefill_measurement(dev, stream, args.steps),
                 "ragged": lambda: ragged_decode_measurement(dev, stream, 128, args.steps),
                 "mtp": lambda: multi_decode_measurement(dev, stream, args.steps),
                 "fp8": lambda: fp8_decode_measurement(dev, stream, args.steps),
                 "paged": lambda: paged_decode_measurement(dev, stream, args.steps),
-                "read": lambda: hbm_read_reference(dev, stream, max(3, args.steps))}[args.only]()
+                "read": lambda: hbm_read_reference(dev, stream, max(3, args.steps)),
+                "mfma": lambda: mfma_rate_reference(
+                    dev, stream, wl.prefill_inputs(wl.GPTOSS_PREFILL)["k"].to(dev),
+                    max(3, args.steps))}[args.only]()
         line["note"] = f"--only {args.only}: this workload alone"
         print(json.dumps(line), flush=True)
         return
@@ -855,6 +912,14 @@ def main():
         for job in jobs:
             res["extra"].append(job())
             log(f"extra line {res['extra'][-1]['workload']} done")
+    if run_p and not args.no_extra:
+        mref = mfma_rate_reference(dev, stream, k)
+        res["mfma_rate_reference"] = mref
+        res["roofline"]["frac_of_measured_mfma"] = round(tflops / mref["value"], 4)
+        for line in res.get("extra", []):
+            if line.get("roofline", {}).get("bound") == "mfma":
+                line["roofline"]["frac_of_measured_mfma"] = round(line["value"] / mref["value"], 4)
+        log("mfma rate reference done")
     if run_d and not args.no_extra:
         ref = hbm_read_reference(dev, stream)
         res["hbm_read_reference"] = ref

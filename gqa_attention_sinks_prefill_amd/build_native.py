@@ -1,5 +1,6 @@
 """Build libsinkattn.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree, and
-the benchmark's streaming-read reference libhbmprobe.so (not part of the library)."""
+the benchmark's reference kernels libbenchprobes.so (a streaming HBM read and a
+plain MFMA loop; not part of the library)."""
 from __future__ import annotations
 
 import os
@@ -24,8 +25,8 @@ SOURCES = ["api.cpp", "prefill.hip", "prefill_d64.hip", "prefill_d128.hip", "dec
 # this kernel), so a source whose extra flags fail to compile is built again
 # without them.
 SOURCE_FLAGS = {"prefill_d64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
-PROBE_LIB = os.path.join(PKG, "libhbmprobe.so")
-PROBE_SOURCES = ["hbm_read_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libbenchprobes.so")
+PROBE_SOURCES = ["hbm_read_probe.hip", "mfma_rate_probe.hip"]
 ARCH = "gfx950"
 
 
