@@ -105,12 +105,19 @@ def measured_traffic(kernel: str):
 
 
 def cpu_model() -> str:
-    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    """The host CPU's model name as lscpu reports it, with its family / model /
+    stepping numbers (a virtualised host may report only the brand), else
+    /proc/cpuinfo's model name."""
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        f = {}
         for ln in out.splitlines():
-            if ln.startswith("Model name:"):
-                return ln.split(":", 1)[1].strip()
+            if ":" in ln:
+                key, val = ln.split(":", 1)
+                f.setdefault(key.strip(), val.strip())
+        if "Model name" in f:
+            ids = ", ".join(f"{k.lower()} {f[k]}" for k in ("CPU family", "Model", "Stepping") if k in f)
+            return f"{f['Model name']} ({ids})" if ids else f["Model name"]
     except (OSError, subprocess.SubprocessError):
         pass
     try:
