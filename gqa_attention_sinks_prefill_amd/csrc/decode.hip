@@ -890,13 +890,26 @@ int decode_split_size(int64_t column_units, int max_len, bool uniform, int head_
   //  * ragged contexts U[1024, 32768] want short ones, the longest requests'
   //    units otherwise finishing alone: B = 1 / 8 ran 17 / 59 us with 1024,
   //    25 / 69 with 2048 (smaller chunks were slower still), B = 32 / 128 191
-  //    / 786 us with 1024, 187 / 745 with 2048, 212 / 801 with 4096.
+  //    / 786 us with 1024, 187 / 745 with 2048, 212 / 801 with 4096;
+  //  * a single request gains from chunks below 1024 tokens once 1024 leaves
+  //    CUs without a unit, up to one unit per CU: 8 KV heads, 4096 / 8192 /
+  //    16384 / 22656 / 32768 tokens ran 13.1 / 12.0 / 14.1 / 16.1 / 19.1 us
+  //    with 384 / 384 / 512 / 768 / 1024-token chunks against 15.9 / 17.2 /
+  //    18.3 / 17.2 / 19.1 with 1024; more units than CUs cost more in set-up
+  //    and merge work than they gain (16384 tokens: 384-token chunks 16.3 us).
   (void)head_dim;
   const int64_t simds = (int64_t)cus * 4;
   auto units = [&](int split) { return column_units * ((max_len + split - 1) / split); };
   if (uniform) {
     int split = 8192;
     while (split > 1024 && (split / 2 >= max_len || units(split) < simds / 4)) split /= 2;
+    if (split == 1024 && units(1024) < simds / 4 && column_units > 0 && column_units <= cus) {
+      // the shortest multiple of 128 tokens (at least 384) that keeps the
+      // units within one per CU
+      const int64_t per = cus / column_units;     // chunks per (request, KV head, slice)
+      const int64_t c = ((max_len + per - 1) / per + 127) / 128 * 128;
+      split = (int)(c < 384 ? 384 : c > 1024 ? 1024 : c);
+    }
     return split;
   }
   return units(2048) >= 4 * simds ? 2048 : 1024;
