@@ -950,6 +950,22 @@ def test_decode_paged_all_rows(P, fp8, q_len, D):
     assert_lse_close(lse.reshape(-1), lse_ref, what=f"{what} lse")
 
 
+@pytest.mark.parametrize("P,split,fp8,D", [(256, 384, False, 64), (256, 384, True, 64),
+                                            (128, 640, False, 128), (512, 896, True, 64)])
+def test_decode_paged_chunks_straddle_pages_all_rows(P, split, fp8, D):
+    """Chunk sizes that are not multiples of the page size (the chunk-size rule
+    picks multiples of 128 below 1024 tokens for a few requests): chunks begin
+    and end inside pages; every row against the oracle."""
+    lens = [0, 1, 383, 384, 385, 511, 512, 513, 767, 768, 1000, 1900]
+    max_ctx = -(-1904 // P) * P
+    inp, kp, vp, bt = _paged_case(lens, 1, 16, 2, D, P, fp8, 170 + P + split + D, max_ctx)
+    out, lse, _ = _paged_gpu(inp, kp, vp, bt, split, fp8)
+    o_ref, lse_ref, _ = _paged_ref(inp, kp, vp, bt, P, fp8)
+    what = f"paged decode P={P} split={split} fp8={fp8} D={D}"
+    assert_close(out.reshape(-1, D), o_ref, what=what)
+    assert_lse_close(lse.reshape(-1), lse_ref, what=f"{what} lse")
+
+
 @pytest.mark.parametrize("B,q_len,fp8", [(128, 1, False), (128, 3, True), (24, 3, False)])
 def test_decode_paged_work_splits(B, q_len, fp8):
     """Each way waves share a chunk (four, one, two) over 16-token pages."""
