@@ -743,7 +743,7 @@ def main():
                     help="run a plain 1 GiB device-to-device copy instead (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
