@@ -297,7 +297,7 @@ def test_decode_ragged_long_context(batch):
     # is dominated by the sink: its output is tiny.
     assert out[:, 63].abs().max().item() < 5e-3
     chosen = sa.sink_attn_decode_split_size(batch, cfg.max_ctx, cfg.num_q_heads, cfg.num_kv_heads,
-                                            cfg.head_dim)
+                                            cfg.head_dim, seq_lens=inp["seq_lens"])
     for split in sorted({cfg.split_size, chosen}):
         out_m, lse_m, (po, pm, pd) = _merged_gpu(inp, split)
         ref_o, ref_lse = (out, lse) if split == cfg.split_size else _decode_gpu(inp, split)[:2]
@@ -310,6 +310,22 @@ def test_decode_ragged_long_context(batch):
             live = max(1, min(ns, -(-L // split)))
             assert torch.isnan(pm[b, ..., live:]).all() and not torch.isnan(pm[b, ..., :live]).any()
         del po, pm, pd
+
+
+@pytest.mark.parametrize("L", [1, 64, 1000, 4096, 8192, 16000, 22656, 32768])
+def test_decode_single_request_library_split(L):
+    """One request at the chunk size the library picks for it (below 1024 tokens
+    when 1024 would leave CUs without a unit): sink_attn_decode_merged bitwise
+    equal to split + merge, and every row against the oracle."""
+    cfg = wl.DecodeConfig("single", 1, L, None, L, 64, 8, 64, (-4.0, 4.0), split_size=1024,
+                          seed=60 + L % 97, edge_sinks={0: float("-inf"), 63: 20.0})
+    inp = wl.decode_inputs(cfg)
+    split = sa.sink_attn_decode_split_size(1, L, 64, 8, 64, seq_lens=inp["seq_lens"])
+    assert split % 128 == 0 and 384 <= split <= 8192
+    out, lse, _ = _decode_gpu(inp, split)
+    out_m, lse_m, _ = _merged_gpu(inp, split)
+    assert _bitwise(out_m[:, 0], out) and torch.equal(lse_m[:, 0], lse), f"L={L} split {split}"
+    _check_decode(inp, out, lse, f"single request L={L} split {split}")
 
 
 @pytest.mark.parametrize("split", [64, 256, 1024, 4096, 8192])
