@@ -892,11 +892,13 @@ int decode_split_size(int64_t column_units, int max_len, bool uniform, int head_
   //    25 / 69 with 2048 (smaller chunks were slower still), B = 32 / 128 191
   //    / 786 us with 1024, 187 / 745 with 2048, 212 / 801 with 4096;
   //  * a single request gains from chunks below 1024 tokens once 1024 leaves
-  //    CUs without a unit, up to one unit per CU: 8 KV heads, 4096 / 8192 /
-  //    16384 / 22656 / 32768 tokens ran 13.1 / 12.0 / 14.1 / 16.1 / 19.1 us
-  //    with 384 / 384 / 512 / 768 / 1024-token chunks against 15.9 / 17.2 /
-  //    18.3 / 17.2 / 19.1 with 1024; more units than CUs cost more in set-up
-  //    and merge work than they gain (16384 tokens: 384-token chunks 16.3 us).
+  //    CUs without a unit, up to one unit per CU: 8 KV heads, 2048 / 4096 /
+  //    8192 / 16384 / 22656 / 32768 tokens ran 10.7 / 10.1 / 11.4 / 14.1 /
+  //    16.1 / 19.1 us with 128 / 128 / 256 / 512 / 768 / 1024-token chunks
+  //    against 14.4 / 15.6 / 17.0 / 18.3 / 17.2 / 19.1 with 1024 (four new
+  //    tokens, FP8 codes and head_dim 128 alike); more units than CUs cost
+  //    more in set-up and merge work than they gain (8192 tokens in 128-token
+  //    chunks: 13.5 us).
   (void)head_dim;
   const int64_t simds = (int64_t)cus * 4;
   auto units = [&](int split) { return column_units * ((max_len + split - 1) / split); };
@@ -904,11 +906,11 @@ int decode_split_size(int64_t column_units, int max_len, bool uniform, int head_
     int split = 8192;
     while (split > 1024 && (split / 2 >= max_len || units(split) < simds / 4)) split /= 2;
     if (split == 1024 && units(1024) < simds / 4 && column_units > 0 && column_units <= cus) {
-      // the shortest multiple of 128 tokens (at least 384) that keeps the
-      // units within one per CU
+      // the shortest multiple of 128 tokens that keeps the units within one
+      // per CU
       const int64_t per = cus / column_units;     // chunks per (request, KV head, slice)
       const int64_t c = ((max_len + per - 1) / per + 127) / 128 * 128;
-      split = (int)(c < 384 ? 384 : c > 1024 ? 1024 : c);
+      split = (int)(c > 1024 ? 1024 : c);
     }
     return split;
   }

@@ -203,7 +203,7 @@ int sink_attn_decode_multi_split(const void* q, int64_t q_stride_b, int64_t q_st
  *    a (request, KV head, column slice, chunk) unit -- long chunks write fewer
  *    chunk states for the merge, and equal units finish together.  When even
  *    1024 leaves fewer units than that (a few requests), the shortest multiple
- *    of 128 tokens, at least 384, that gives at most one unit per CU.
+ *    of 128 tokens that gives at most one unit per CU.
  *  - Otherwise (ragged or unknown lengths): 1024, or 2048 when chunks of 2048
  *    at max_ctx still give every SIMD four units -- short chunks keep a
  *    ragged batch's longest requests from finishing alone.

@@ -512,7 +512,7 @@ def test_decode_split_size_follows_the_launch_shape():
             for q_len, hq, hkv, d in ((1, 64, 8, 64), (4, 64, 8, 64), (1, 64, 4, 128)):
                 for lens in (None, [max_ctx] * batch, [max_ctx // (b + 1) for b in range(batch)]):
                     s = sa.sink_attn_decode_split_size(batch, max_ctx, hq, hkv, d, q_len, lens)
-                    assert s in (1024, 2048, 4096, 8192) or (s % 128 == 0 and 384 <= s < 1024)
+                    assert s in (1024, 2048, 4096, 8192) or (s % 128 == 0 and 128 <= s < 1024)
     split = sa.sink_attn_decode_split_size
     # ragged or unknown lengths: 1024, or 2048 for many long requests
     assert split(64, 8192, 64, 8, 64) == 1024
@@ -534,14 +534,15 @@ def test_decode_split_size_follows_the_launch_shape():
     assert split(64, 8192, 64, 8, 64, seq_lens=[5000] * 64) == 8192
     assert split(64, 8192, 64, 8, 64, seq_lens=[3000] * 64) == 4096
     # a few equal requests that leave CUs idle at 1024: the shortest multiple of
-    # 128 (>= 384) giving at most one (request, KV head, chunk) unit per CU
+    # 128 giving at most one (request, KV head, chunk) unit per CU
     assert split(1, 32768, 64, 8, 64, seq_lens=[22656]) == 768      # 30 chunks x 8 heads
     assert split(1, 16384, 64, 8, 64, seq_lens=[16384]) == 512      # 32 x 8 = 256
     assert split(1, 16384, 64, 8, 64, seq_lens=[16000]) == 512
-    assert split(1, 8192, 64, 8, 64, seq_lens=[8192]) == 384        # 256 would give 32 x 8
-    assert split(1, 1000, 64, 8, 64, seq_lens=[1000]) == 384
+    assert split(1, 8192, 64, 8, 64, seq_lens=[8192]) == 256        # 32 x 8 = 256
+    assert split(1, 1000, 64, 8, 64, seq_lens=[1000]) == 128
+    assert split(1, 4096, 64, 8, 64, seq_lens=[4096]) == 128        # 32 x 8
     assert split(2, 16384, 64, 8, 64, seq_lens=[16384] * 2) == 1024  # 1024 already fills the CUs
-    assert split(1, 16384, 64, 4, 128, seq_lens=[16384]) == 384      # 4 KV heads: 256 would fit
+    assert split(1, 16384, 64, 4, 128, seq_lens=[16384]) == 256      # 4 KV heads: 64 x 4
     assert split(1, 32768, 64, 8, 64) == 1024                        # lengths unknown: ragged rule
 
 def _noalloc(**kw):

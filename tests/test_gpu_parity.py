@@ -321,7 +321,7 @@ def test_decode_single_request_library_split(L):
                           seed=60 + L % 97, edge_sinks={0: float("-inf"), 63: 20.0})
     inp = wl.decode_inputs(cfg)
     split = sa.sink_attn_decode_split_size(1, L, 64, 8, 64, seq_lens=inp["seq_lens"])
-    assert split % 128 == 0 and 384 <= split <= 8192
+    assert split % 128 == 0 and 128 <= split <= 8192
     out, lse, _ = _decode_gpu(inp, split)
     out_m, lse_m, _ = _merged_gpu(inp, split)
     assert _bitwise(out_m[:, 0], out) and torch.equal(lse_m[:, 0], lse), f"L={L} split {split}"
